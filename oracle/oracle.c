@@ -1,0 +1,242 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for one sparse MoE layer's routed expert
+ * FFN over a whole prompt, as described in "EStream: Fast and Memory-Efficient
+ * MoE Prefill through Expert Virtualization on Mobile NPUs" (arXiv 2609.06551),
+ * section 3.2 "Intra-NPU MoE Execution".
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library. The GPU library never
+ * links, loads or calls it, and it shares no code, header or table with it.
+ *
+ * Every function computes its result from the definition, with no blocking,
+ * fusion or reordering:
+ *   oracle_router_logits  L = X W_r (+ bias), fp32, one fused multiply-add
+ *                         per term in ascending hidden index.  The top-k
+ *                         decision is taken on these fp32 values, so the order
+ *                         of the chain is part of the contract.
+ *   oracle_topk           top-k of E experts per token (section 2.2: "a router
+ *                         assigns each token to the top-k of E experts"), ties
+ *                         to the lower expert id; softmax weights in fp64,
+ *                         optionally renormalised over the k selected; shared
+ *                         experts appended with weight 1.
+ *   oracle_route_map      the route map of Algorithm 1: slot resolve psi_i =
+ *                         Phi(e_i), per-slot counts, prefix-sum offsets, and a
+ *                         cursor pass in ascending route index storing (t_i, i).
+ *   oracle_expert_ffn     Eq. (2) Y_t = A_t + sum alpha F_e(X_t) with Eq. (1)
+ *                         F_e(x) = W_d (SiLU(W_g x) * (W_u x)), per token and
+ *                         per selected expert, accumulated in fp64.
+ *
+ * Parity status: every function is pinned by CPU tests (brute force, closed
+ * forms, special cases and invariants); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/*
+ * Router logits. L[t][e] = sum over i = 0..d-1 of X[t][i] * Wr[i][e], evaluated
+ * as acc = fmaf(X[t][i], Wr[i][e], acc) for ascending i from acc = 0.0f, then
+ * L = acc + bias[e] (one fp32 addition) when a bias is given.
+ * X: [T][ldx] fp32 values (bf16 inputs widened exactly), Wr: [d][E], bias: [E]
+ * or NULL, L: [T][E].
+ */
+void oracle_router_logits(int64_t T, int64_t d, int64_t E, const float *X,
+                          int64_t ldx, const float *Wr, const float *bias,
+                          float *L)
+{
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        for (int64_t e = 0; e < E; ++e) {
+            float acc = 0.0f;
+            for (int64_t i = 0; i < d; ++i)
+                acc = fmaf(X[t * ldx + i], Wr[i * E + e], acc);
+            if (bias) acc = acc + bias[e];
+            L[t * E + e] = acc;
+        }
+    }
+}
+
+/*
+ * Top-k routing for each token t.
+ *   idx[t][j], j < k: the j-th choice by repeated selection of the largest
+ *     logit among the experts not yet chosen; equal logits go to the lower id.
+ *   alpha: p_e = exp(L_e - m) / sum_e' exp(L_e' - m) with m = max_e L_e
+ *     (the softmax over all E), in fp64; alpha[t][j] = p_{idx[t][j]}, divided
+ *     by sum_{j'<k} p_{idx[t][j']} when renorm != 0.
+ *   shared experts: idx[t][k + s] = E + s, alpha = 1, for s < n_shared.
+ * idx and alpha are [T][k + n_shared].
+ */
+void oracle_topk(int64_t T, int64_t E, int64_t k, int64_t n_shared, int renorm,
+                 const float *L, int32_t *idx, double *alpha)
+{
+    const int64_t kp = k + n_shared;
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        const float *l = L + t * E;
+        unsigned char *taken = (unsigned char *)calloc((size_t)E, 1);
+        double *p = (double *)malloc(sizeof(double) * (size_t)E);
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e;  /* strict: ties keep lower id */
+            }
+            taken[best] = 1;
+            idx[t * kp + j] = (int32_t)best;
+        }
+        double m = (double)l[0];
+        for (int64_t e = 1; e < E; ++e)
+            if ((double)l[e] > m) m = (double)l[e];
+        double s = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            p[e] = exp((double)l[e] - m);
+            s += p[e];
+        }
+        for (int64_t e = 0; e < E; ++e) p[e] = p[e] / s;
+        double sel = 0.0;
+        for (int64_t j = 0; j < k; ++j) sel += p[idx[t * kp + j]];
+        for (int64_t j = 0; j < k; ++j) {
+            double a = p[idx[t * kp + j]];
+            alpha[t * kp + j] = renorm ? a / sel : a;
+        }
+        for (int64_t s2 = 0; s2 < n_shared; ++s2) {
+            idx[t * kp + k + s2] = (int32_t)(E + s2);
+            alpha[t * kp + k + s2] = 1.0;
+        }
+        free(taken);
+        free(p);
+    }
+}
+
+/*
+ * Route map of Algorithm 1 (section 3.2, "Composed Sparse Route and Parameter
+ * Binding") for the routes of tokens t0 .. t0+nt-1.  Route i = t*kp + j sends
+ * token t to logical expert e_i = idx[i].
+ *   psi_i = phi[e_i] (-1 = not resident; such routes are left out);
+ *   count[s] = number of routes with psi_i = s, s < P;
+ *   offset[0] = 0, offset[s+1] = offset[s] + count[s];
+ *   cursor = offset; for i ascending: p = cursor[psi_i]; rec[p] = (t_i, i);
+ *   cursor[psi_i] = p + 1.
+ * route_pos[i] = p for placed routes and -1 for left-out routes of the range;
+ * entries outside the range are not touched.  Returns n_valid = offset[P], or
+ * -1 if an expert id is outside [0, n_exp) or phi names a slot outside
+ * [-1, P).
+ */
+int64_t oracle_route_map(int64_t kp, int64_t t0, int64_t nt, const int32_t *idx,
+                         int64_t n_exp, const int32_t *phi, int64_t P,
+                         int32_t *count, int32_t *offset, int32_t *rec_token,
+                         int32_t *rec_route, int32_t *route_pos)
+{
+    const int64_t i0 = t0 * kp, i1 = (t0 + nt) * kp;
+    for (int64_t i = i0; i < i1; ++i) {
+        if (idx[i] < 0 || idx[i] >= n_exp) return -1;
+        if (phi[idx[i]] < -1 || phi[idx[i]] >= P) return -1;
+    }
+    for (int64_t s = 0; s < P; ++s) count[s] = 0;
+    for (int64_t i = i0; i < i1; ++i) {
+        int32_t psi = phi[idx[i]];
+        if (psi >= 0) count[psi] += 1;
+    }
+    offset[0] = 0;
+    for (int64_t s = 0; s < P; ++s) offset[s + 1] = offset[s] + count[s];
+    int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)(P + 1));
+    for (int64_t s = 0; s <= P; ++s) cursor[s] = offset[s];
+    for (int64_t i = i0; i < i1; ++i) {
+        int32_t psi = phi[idx[i]];
+        if (psi < 0) {
+            route_pos[i] = -1;
+            continue;
+        }
+        int32_t p = cursor[psi];
+        rec_token[p] = (int32_t)(i / kp);
+        rec_route[p] = (int32_t)i;
+        route_pos[i] = p;
+        cursor[psi] = p + 1;
+    }
+    free(cursor);
+    return offset[P];
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * Expert FFN and weighted combine for the listed tokens, Eq. (1)-(2):
+ *   y = A[t]; for j = 0 .. kp-1 (routes of token t whose mask byte is nonzero,
+ *   all of them when route_mask is NULL), with e = idx[t][j]:
+ *     g[n] = sum_i Wg[e][n][i] x[i],  u[n] = sum_i Wu[e][n][i] x[i]   (n < f)
+ *     h[n] = SiLU(g[n]) * u[n],       SiLU(z) = z / (1 + exp(-z))
+ *     o[m] = sum_n Wd[e][m][n] h[n]                                   (m < d)
+ *     y[m] += alpha[t][j] * o[m]
+ * in fp64.  X: [T][ldx] fp32 values; Wg, Wu: [n_exp][f][d]; Wd: [n_exp][d][f];
+ * A: [T][d] fp32 or NULL (zero residual); Y: [n_tok][d] fp64, row r for token
+ * tokens[r].  route_mask is indexed by the global route id t*kp + j.
+ */
+void oracle_expert_ffn(int64_t d, int64_t f, int64_t kp, int64_t n_tok,
+                       const int64_t *tokens, const float *X, int64_t ldx,
+                       const int32_t *idx, const double *alpha,
+                       const unsigned char *route_mask, const float *Wg,
+                       const float *Wu, const float *Wd, const float *A,
+                       double *Y)
+{
+    int64_t r;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < n_tok; ++r) {
+        const int64_t t = tokens[r];
+        const float *x = X + t * ldx;
+        double *y = Y + r * d;
+        double *g = (double *)malloc(sizeof(double) * (size_t)f);
+        double *u = (double *)malloc(sizeof(double) * (size_t)f);
+        double *h = (double *)malloc(sizeof(double) * (size_t)f);
+        for (int64_t m = 0; m < d; ++m) y[m] = A ? (double)A[t * d + m] : 0.0;
+        for (int64_t j = 0; j < kp; ++j) {
+            const int64_t i = t * kp + j;
+            if (route_mask && !route_mask[i]) continue;
+            const int64_t e = idx[i];
+            const float *wg = Wg + e * f * d;
+            const float *wu = Wu + e * f * d;
+            const float *wd = Wd + e * d * f;
+            for (int64_t n = 0; n < f; ++n) {
+                double sg = 0.0, su = 0.0;
+                for (int64_t c = 0; c < d; ++c) {
+                    sg += (double)wg[n * d + c] * (double)x[c];
+                    su += (double)wu[n * d + c] * (double)x[c];
+                }
+                g[n] = sg;
+                u[n] = su;
+            }
+            for (int64_t n = 0; n < f; ++n) h[n] = silu(g[n]) * u[n];
+            for (int64_t m = 0; m < d; ++m) {
+                double o = 0.0;
+                for (int64_t n = 0; n < f; ++n) o += (double)wd[m * f + n] * h[n];
+                y[m] += alpha[i] * o;
+            }
+        }
+        free(g);
+        free(u);
+        free(h);
+    }
+}

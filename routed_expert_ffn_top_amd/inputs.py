@@ -1,0 +1,196 @@
+"""Seeded synthetic inputs for the routed-expert MoE layer workloads.
+
+This module is the only code that both the HIP path and the CPU oracle use.
+It draws random tensors and nothing else: no step of the layer's arithmetic
+(router, top-k, descriptors, projections, combine) lives here.
+
+Workloads (shapes of the EStream evaluation models; the pages' C4 prompts and
+trained checkpoints are replaced by random data of the same shape):
+
+* ``tiny_fp32``      T=64, d=128, E=8, k=2, f=256, fp32, renormalised top-2.
+* ``olmoe``          OLMoE-1B-7B-shaped layer: d=2048, E=64, k=8, f=1024, bf16,
+                     renormalised top-8 (T=1024 by default, also T=4096).
+* ``dsv2lite``       DeepSeek-V2-Lite-shaped layer: d=2048, 64 routed experts,
+                     top-6 not renormalised, plus 2 always-on shared experts,
+                     f=1408, bf16, T=4096.
+* ``mixtral``        Mixtral-8x7B-shaped layer: d=4096, E=8, k=2, f=14336,
+                     bf16, renormalised top-2, T in {256, 1024, 4096}.
+* ``virt_olmoe``     the OLMoE shape with a Zipf(1.1) popularity bias on the
+                     router logits and a P=16 slot arena (expert paging).
+
+Distributions: X ~ N(0,1); W_gate, W_up, W_down, W_router ~ N(0, 0.02^2)
+(0.02 is the standard deviation); residual A ~ N(0,1) for parity runs and 0
+for timed runs. Values are drawn in fp32 from a seeded torch generator and,
+for bf16 workloads, rounded to bf16 (round to nearest even) so that the GPU
+and the oracle see exactly the same numbers. The router weight stays fp32.
+
+Weight layout is nn.Linear style ([out, in]): W_gate, W_up [n_exp, f, d],
+W_down [n_exp, d, f], with n_exp = E + n_shared (shared experts last).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+STD_W = 0.02
+ZIPF_S = 1.1
+
+
+@dataclasses.dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int
+    d: int
+    E: int
+    k: int
+    f: int
+    n_shared: int = 0
+    dtype: str = "bf16"          # "bf16" or "f32": X, expert weights, H
+    renorm: bool = True          # renormalise the top-k softmax weights
+    zipf: bool = False           # Zipf(1.1) popularity bias on the logits
+    P: Optional[int] = None      # arena slots (None: one slot per expert)
+    G: int = 8                   # slots per bank when paging
+    index: int = 0               # workload number used in the seed
+
+    @property
+    def n_exp(self) -> int:
+        return self.E + self.n_shared
+
+    @property
+    def kp(self) -> int:
+        """Routes per token: k routed plus the shared experts."""
+        return self.k + self.n_shared
+
+    @property
+    def slots(self) -> int:
+        return self.P if self.P is not None else self.n_exp
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def with_(self, **kw) -> "MoEConfig":
+        return dataclasses.replace(self, **kw)
+
+    def flops(self) -> int:
+        """Algorithmic expert FLOPs: 6*d*f per route (gate+up 4df, down 2df)."""
+        return 6 * self.T * self.kp * self.d * self.f
+
+    def router_flops(self) -> int:
+        return 2 * self.T * self.d * self.E
+
+
+def _cfg(name, index, **kw) -> MoEConfig:
+    return MoEConfig(name=name, index=index, **kw)
+
+
+CONFIGS = {
+    "tiny_fp32": _cfg("tiny_fp32", 1, T=64, d=128, E=8, k=2, f=256, dtype="f32"),
+    "olmoe_t1024": _cfg("olmoe_t1024", 2, T=1024, d=2048, E=64, k=8, f=1024),
+    "olmoe_t4096": _cfg("olmoe_t4096", 2, T=4096, d=2048, E=64, k=8, f=1024),
+    "dsv2lite_t4096": _cfg("dsv2lite_t4096", 3, T=4096, d=2048, E=64, k=6,
+                           f=1408, n_shared=2, renorm=False),
+    "mixtral_t256": _cfg("mixtral_t256", 4, T=256, d=4096, E=8, k=2, f=14336),
+    "mixtral_t1024": _cfg("mixtral_t1024", 4, T=1024, d=4096, E=8, k=2, f=14336),
+    "mixtral_t4096": _cfg("mixtral_t4096", 4, T=4096, d=4096, E=8, k=2, f=14336),
+}
+for _t in (256, 512, 1024, 2048, 4096):
+    CONFIGS[f"virt_olmoe_t{_t}"] = _cfg(f"virt_olmoe_t{_t}", 5, T=_t, d=2048,
+                                        E=64, k=8, f=1024, zipf=True, P=16, G=8)
+
+
+def seed_for(cfg: MoEConfig, layer: int = 0) -> int:
+    return 1000 * cfg.index + layer
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    cfg: MoEConfig
+    X: torch.Tensor               # [T, d]        cfg dtype
+    Wr: torch.Tensor              # [d, E]        fp32
+    bias: Optional[torch.Tensor]  # [E]           fp32 (Zipf workloads) or None
+    Wg: torch.Tensor              # [n_exp, f, d] cfg dtype
+    Wu: torch.Tensor              # [n_exp, f, d] cfg dtype
+    Wd: torch.Tensor              # [n_exp, d, f] cfg dtype
+    A: torch.Tensor               # [T, d]        fp32 residual
+
+    def to(self, device) -> "LayerInputs":
+        mv = lambda t: None if t is None else t.to(device)
+        return LayerInputs(self.cfg, mv(self.X), mv(self.Wr), mv(self.bias),
+                           mv(self.Wg), mv(self.Wu), mv(self.Wd), mv(self.A))
+
+
+def _normal(gen, shape, std, device):
+    t = torch.empty(shape, dtype=torch.float32, device=device)
+    t.normal_(0.0, std, generator=gen)
+    return t
+
+
+def zipf_bias(cfg: MoEConfig, gen: torch.Generator, device) -> torch.Tensor:
+    """Log-popularity bias: p_e proportional to rank_e^(-1.1), rank = 1 + a
+    seeded permutation of the expert ids; returns ln p_e as fp32."""
+    perm = torch.randperm(cfg.E, generator=gen, device=device)
+    rank = (perm + 1).to(torch.float64)
+    w = rank.pow(-ZIPF_S)
+    return torch.log(w / w.sum()).to(torch.float32)
+
+
+def make_inputs(cfg: MoEConfig, layer: int = 0, device="cpu",
+                residual: bool = True, seed: Optional[int] = None) -> LayerInputs:
+    """Draw one layer's inputs. Same (cfg, layer, device) -> same values."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed_for(cfg, layer) if seed is None else seed)
+    dt = cfg.torch_dtype
+    X = _normal(gen, (cfg.T, cfg.d), 1.0, device).to(dt)
+    Wr = _normal(gen, (cfg.d, cfg.E), STD_W, device)
+    ne = cfg.n_exp
+    Wg = _normal(gen, (ne, cfg.f, cfg.d), STD_W, device).to(dt)
+    Wu = _normal(gen, (ne, cfg.f, cfg.d), STD_W, device).to(dt)
+    Wd = _normal(gen, (ne, cfg.d, cfg.f), STD_W, device).to(dt)
+    if residual:
+        A = _normal(gen, (cfg.T, cfg.d), 1.0, device)
+    else:
+        A = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device=device)
+    bias = zipf_bias(cfg, gen, device) if cfg.zipf else None
+    return LayerInputs(cfg, X, Wr, bias, Wg, Wu, Wd, A)
+
+
+def make_logits(T: int, E: int, seed: int, scale: float = 1.0,
+                device="cpu") -> torch.Tensor:
+    """Random fp32 router logits for tests that pass logits in directly."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return _normal(gen, (T, E), scale, torch.device(device))
+
+
+def identity_phi(n_exp: int) -> torch.Tensor:
+    return torch.arange(n_exp, dtype=torch.int32)
+
+
+def random_phi(n_exp: int, P: int, seed: int, n_absent: int = 0) -> torch.Tensor:
+    """A random injective placement map: n_exp - n_absent experts get distinct
+    slots in [0, P); the rest are absent (-1)."""
+    gen = torch.Generator().manual_seed(seed)
+    assert n_exp - n_absent <= P
+    experts = torch.randperm(n_exp, generator=gen)
+    slots = torch.randperm(P, generator=gen)
+    phi = torch.full((n_exp,), -1, dtype=torch.int32)
+    for j in range(n_exp - n_absent):
+        phi[experts[j]] = slots[j].to(torch.int32)
+    return phi
+
+
+def rows_per_slot_stats(counts) -> dict:
+    c = [int(x) for x in counts]
+    nz = [x for x in c if x > 0]
+    return {"slots": len(c), "active": len(nz), "max": max(c) if c else 0,
+            "min_active": min(nz) if nz else 0,
+            "mean": (sum(c) / len(c)) if c else 0.0}
+
+
+__all__ = ["MoEConfig", "CONFIGS", "LayerInputs", "make_inputs", "make_logits",
+           "seed_for", "identity_phi", "random_phi", "zipf_bias", "STD_W",
+           "rows_per_slot_stats"]

@@ -1,0 +1,370 @@
+"""Checks that pin the CPU oracle to facts other than itself.
+
+Each ``check_*`` takes an ``Oracle`` (any build of oracle.c) and raises
+AssertionError when the oracle disagrees with:
+
+* hand-worked closed forms (tests/golden/*.json);
+* exact integer arithmetic (router on inputs whose fp32 sums are exact);
+* the fp64 error bound of recursive summation;
+* a numpy/scipy brute force of a *different* formulation: top-k by lexsort,
+  softmax by scipy, the route map by a stable argsort and bincount, and the
+  layer as a dense masked sum over every expert on every token;
+* special cases (k=1 argmax, k=E full order, k=2 logistic weights, E=1 dense
+  SwiGLU, W_up = 0, W_down scaled by 2, expert relabelling, hidden-unit
+  permutation, masked routes).
+
+The mutation test runs all of them against oracle builds with planted
+mistakes and requires every mistake to be caught.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+from scipy.special import softmax, expit
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def _bf16_values(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest even) and widen back to fp32."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _layer_weights(rng, ne, d, f, std=0.02, bf16=True):
+    Wg = rng.standard_normal((ne, f, d), dtype=np.float32) * np.float32(std)
+    Wu = rng.standard_normal((ne, f, d), dtype=np.float32) * np.float32(std)
+    Wd = rng.standard_normal((ne, d, f), dtype=np.float32) * np.float32(std)
+    if bf16:
+        Wg, Wu, Wd = _bf16_values(Wg), _bf16_values(Wu), _bf16_values(Wd)
+    return Wg, Wu, Wd
+
+
+def _random_routes(rng, T, E, k, n_shared=0):
+    """Distinct random experts per token and random positive weights."""
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    if n_shared:
+        sh = np.tile(np.arange(E, E + n_shared, dtype=np.int32), (T, 1))
+        idx = np.concatenate([idx, sh], axis=1)
+    alpha = rng.uniform(0.05, 1.0, size=idx.shape)
+    return idx, alpha
+
+
+def dense_brute_force(X, idx, alpha, Wg, Wu, Wd, A=None, route_mask=None):
+    """Every expert on every token in fp64 (matrix form), masked by routing."""
+    X = X.astype(np.float64)
+    T, d = X.shape
+    ne = Wg.shape[0]
+    M = np.zeros((T, ne))
+    kp = idx.shape[1]
+    for t in range(T):
+        for j in range(kp):
+            if route_mask is None or route_mask[t * kp + j]:
+                M[t, idx[t, j]] += alpha[t, j]
+    Y = np.zeros((T, d)) if A is None else A.astype(np.float64).copy()
+    for e in range(ne):
+        G = X @ Wg[e].astype(np.float64).T
+        U = X @ Wu[e].astype(np.float64).T
+        H = G * expit(G) * U
+        O = H @ Wd[e].astype(np.float64).T
+        Y += M[:, e:e + 1] * O
+    return Y
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------- router --
+def check_router_golden(orc):
+    for case in _load("router_chain.json")["cases"]:
+        x = np.array([case["x"]], dtype=np.float32)
+        w = np.array(case["w"], dtype=np.float32)[:, None]
+        b = np.array([case["bias"]], dtype=np.float32)
+        L = orc.router_logits(x, w, b)
+        assert L[0, 0] == np.float32(case["expect"]), (case["why"], L[0, 0])
+
+
+def check_router_exact_integers(orc):
+    """Small integers scaled by 2^-4: every fp32 partial sum is exact, so
+    the logits equal the exact integer matrix product."""
+    rng = _rng(11)
+    T, d, E = 17, 64, 8
+    Xi = rng.integers(-8, 9, size=(T, d))
+    Wi = rng.integers(-8, 9, size=(d, E))
+    bi = rng.integers(-8, 9, size=E)
+    X = Xi.astype(np.float32)
+    Wr = (Wi.astype(np.float32) / 16).astype(np.float32)
+    b = (bi.astype(np.float32) / 16).astype(np.float32)
+    L = orc.router_logits(X, Wr, b)
+    exact = (Xi @ Wi + bi[None, :]) / 16.0
+    assert np.array_equal(L.astype(np.float64), exact)
+    L0 = orc.router_logits(X, Wr, None)
+    assert np.array_equal(L0.astype(np.float64), (Xi @ Wi) / 16.0)
+
+
+def check_router_error_bound(orc):
+    """|L - exact| <= gamma_d * sum|x w| + |bias rounding| (recursive sum)."""
+    rng = _rng(12)
+    T, d, E = 9, 2048, 64
+    X = _bf16_values(rng.standard_normal((T, d), dtype=np.float32))
+    Wr = rng.standard_normal((d, E), dtype=np.float32) * np.float32(0.02)
+    L = orc.router_logits(X, Wr, None).astype(np.float64)
+    exact = X.astype(np.float64) @ Wr.astype(np.float64)
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    bound = gamma * (np.abs(X.astype(np.float64)) @ np.abs(Wr.astype(np.float64)))
+    assert np.all(np.abs(L - exact) <= bound)
+
+
+# ----------------------------------------------------------------- top-k --
+def _lexsort_topk(L, k):
+    T, E = L.shape
+    out = np.empty((T, k), dtype=np.int32)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -L[t].astype(np.float64)))
+        out[t] = order[:k]
+    return out
+
+
+def check_topk_bruteforce(orc):
+    rng = _rng(21)
+    for (T, E, k) in [(50, 64, 8), (40, 8, 2), (30, 64, 6), (20, 5, 5), (25, 7, 1)]:
+        L = rng.standard_normal((T, E), dtype=np.float32)
+        idx, _ = orc.topk(L, k, 0, True)
+        assert np.array_equal(idx, _lexsort_topk(L, k)), (T, E, k)
+        # heavy ties: logits drawn from 3 values
+        Lt = rng.integers(0, 3, size=(T, E)).astype(np.float32)
+        idx, _ = orc.topk(Lt, k, 0, True)
+        assert np.array_equal(idx, _lexsort_topk(Lt, k)), ("ties", T, E, k)
+
+
+def check_topk_special(orc):
+    rng = _rng(22)
+    L = rng.standard_normal((33, 16), dtype=np.float32)
+    idx, _ = orc.topk(L, 1, 0, True)
+    assert np.array_equal(idx[:, 0], np.argmax(L, axis=1))
+    idx, _ = orc.topk(L, 16, 0, True)
+    for t in range(33):
+        assert np.array_equal(idx[t], np.argsort(-L[t].astype(np.float64), kind="stable"))
+    # hand example with ties: [1, 3, 3, 2, 3] -> 1, 2, 4, then 3
+    h = np.array([[1.0, 3.0, 3.0, 2.0, 3.0]], dtype=np.float32)
+    idx, al = orc.topk(h, 4, 0, False)
+    assert idx.tolist() == [[1, 2, 4, 3]]
+    z = math.exp(1) + 3 * math.exp(3) + math.exp(2)
+    assert abs(al[0, 0] - math.exp(3) / z) < 1e-15
+    assert abs(al[0, 3] - math.exp(2) / z) < 1e-15
+
+
+def check_alpha(orc):
+    rng = _rng(23)
+    T, E = 40, 64
+    L = rng.standard_normal((T, E), dtype=np.float32)
+    sm = softmax(L.astype(np.float64), axis=1)
+    for k in (1, 6, 8):
+        idx, al = orc.topk(L, k, 0, False)
+        ref = np.take_along_axis(sm, idx.astype(np.int64), axis=1)
+        assert np.max(np.abs(al - ref)) < 1e-14
+        idx, al = orc.topk(L, k, 0, True)
+        assert np.max(np.abs(al.sum(axis=1) - 1.0)) < 1e-14
+        # renormalised ratios equal the exponentiated logit differences
+        r = al[:, 0:1] / al
+        lsel = np.take_along_axis(L.astype(np.float64), idx.astype(np.int64), axis=1)
+        assert np.max(np.abs(r - np.exp(lsel[:, 0:1] - lsel)) / r) < 1e-13
+    # k = E renormalised is the full softmax in rank order
+    idx, al = orc.topk(L, E, 0, True)
+    assert np.max(np.abs(al - np.take_along_axis(sm, idx.astype(np.int64), 1))) < 1e-14
+    # top-2 renormalised: weight of the first choice = logistic(L1 - L2)
+    L8 = rng.standard_normal((T, 8), dtype=np.float32)
+    idx, al = orc.topk(L8, 2, 0, True)
+    l = np.take_along_axis(L8.astype(np.float64), idx.astype(np.int64), axis=1)
+    assert np.max(np.abs(al[:, 0] - expit(l[:, 0] - l[:, 1]))) < 1e-14
+
+
+def check_shared(orc):
+    rng = _rng(24)
+    L = rng.standard_normal((12, 64), dtype=np.float32)
+    idx, al = orc.topk(L, 6, 2, False)
+    assert idx.shape == (12, 8)
+    assert np.all(idx[:, 6] == 64) and np.all(idx[:, 7] == 65)
+    assert np.all(al[:, 6:] == 1.0)
+    i2, a2 = orc.topk(L, 6, 0, False)
+    assert np.array_equal(idx[:, :6], i2) and np.array_equal(al[:, :6], a2)
+
+
+# ------------------------------------------------------------- route map --
+def _route_map_brute(idx, phi, P, t0, nt):
+    T, kp = idx.shape
+    routes = np.arange(t0 * kp, (t0 + nt) * kp)
+    psi = phi[idx.reshape(-1)[routes]]
+    valid = routes[psi >= 0]
+    pv = psi[psi >= 0]
+    order = np.argsort(pv, kind="stable")
+    rec_route = valid[order]
+    count = np.bincount(pv, minlength=P)
+    offset = np.concatenate([[0], np.cumsum(count)])
+    pos = np.full(T * kp, -7, dtype=np.int64)
+    pos[routes] = -1
+    pos[rec_route] = np.arange(len(rec_route))
+    return dict(count=count, offset=offset, rec_route=rec_route,
+                rec_token=rec_route // kp, route_pos=pos, n_valid=len(rec_route))
+
+
+def check_route_map_golden(orc):
+    g = _load("route_map_hand.json")
+    ex = g["expect"]
+    r = orc.route_map(np.array(g["idx"]), np.array(g["phi"]), g["P"])
+    for key in ("count", "offset", "rec_token", "rec_route", "route_pos"):
+        assert r[key].tolist() == ex[key], key
+    assert r["n_valid"] == ex["n_valid"]
+
+
+def check_route_map_bruteforce(orc):
+    rng = _rng(31)
+    for (T, E, k, P, absent, t0, nt) in [(100, 64, 8, 64, 0, 0, 100),
+                                         (64, 8, 2, 8, 0, 0, 64),
+                                         (77, 66, 8, 40, 26, 0, 77),
+                                         (50, 64, 8, 16, 48, 10, 25),
+                                         (1, 8, 2, 8, 0, 0, 1)]:
+        idx, _ = _random_routes(rng, T, E, k)
+        perm = rng.permutation(E)
+        phi = np.full(E, -1, dtype=np.int32)
+        slots = rng.permutation(P)
+        for j in range(E - absent):
+            phi[perm[j]] = slots[j]
+        pos0 = np.full(T * k, -7, dtype=np.int32)
+        r = orc.route_map(idx, phi, P, t0, nt, route_pos=pos0)
+        b = _route_map_brute(idx, phi, P, t0, nt)
+        assert np.array_equal(r["count"], b["count"])
+        assert np.array_equal(r["offset"], b["offset"])
+        assert np.array_equal(r["rec_route"], b["rec_route"])
+        assert np.array_equal(r["rec_token"], b["rec_token"])
+        assert np.array_equal(r["route_pos"], b["route_pos"])
+        assert r["n_valid"] == b["n_valid"]
+        # invariants: counts sum to the placed routes; offsets monotone;
+        # every placed (token, rank) appears once; ascending inside a slot
+        assert r["count"].sum() == r["n_valid"] == r["offset"][-1]
+        assert np.all(np.diff(r["offset"]) >= 0) and r["offset"][0] == 0
+        assert len(set(r["rec_route"].tolist())) == r["n_valid"]
+        for s in range(P):
+            seg = r["rec_route"][r["offset"][s]:r["offset"][s + 1]]
+            assert np.all(np.diff(seg) > 0)
+            assert np.all(phi[idx.reshape(-1)[seg]] == s)
+    # full identity map: every route placed, counts sum to T*k
+    idx, _ = _random_routes(rng, 64, 64, 8)
+    r = orc.route_map(idx, np.arange(64, dtype=np.int32), 64)
+    assert r["n_valid"] == 64 * 8
+
+
+def check_route_map_errors(orc):
+    idx = np.array([[0, 9]], dtype=np.int32)
+    try:
+        orc.route_map(idx, np.arange(4, dtype=np.int32), 4)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("expert id out of range accepted")
+    try:
+        orc.route_map(np.array([[0, 1]], dtype=np.int32),
+                      np.array([0, 5], dtype=np.int32), 4)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("slot out of range accepted")
+
+
+# ------------------------------------------------------------------- FFN --
+def check_ffn_dense_bruteforce(orc):
+    rng = _rng(41)
+    for (T, d, f, E, k, S) in [(24, 64, 96, 8, 2, 0), (16, 128, 64, 6, 3, 2)]:
+        X = _bf16_values(rng.standard_normal((T, d), dtype=np.float32))
+        A = rng.standard_normal((T, d), dtype=np.float32)
+        Wg, Wu, Wd = _layer_weights(rng, E + S, d, f, std=0.1)
+        idx, alpha = _random_routes(rng, T, E, k, S)
+        Y = orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, A)
+        ref = dense_brute_force(X, idx, alpha, Wg, Wu, Wd, A)
+        assert _rel(Y, ref) < 1e-12, _rel(Y, ref)
+        # a token subset returns the same rows
+        sub = np.array([5, 0, T - 1])
+        Ys = orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, A, tokens=sub)
+        assert np.array_equal(Ys, Y[sub])
+        # masked routes are left out of the sum
+        mask = rng.integers(0, 2, size=T * (k + S)).astype(np.uint8)
+        Ym = orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, A, route_mask=mask)
+        refm = dense_brute_force(X, idx, alpha, Wg, Wu, Wd, A, route_mask=mask)
+        assert _rel(Ym, refm) < 1e-12
+
+
+def check_ffn_special(orc):
+    rng = _rng(42)
+    T, d, f = 10, 32, 48
+    X = rng.standard_normal((T, d), dtype=np.float32)
+    A = rng.standard_normal((T, d), dtype=np.float32)
+    Wg, Wu, Wd = _layer_weights(rng, 1, d, f, std=0.2, bf16=False)
+    # E = 1, k = 1: the textbook dense SwiGLU FFN, y = A + W2 (silu(W1 x) * (W3 x))
+    idx = np.zeros((T, 1), dtype=np.int32)
+    alpha = np.ones((T, 1))
+    Y = orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, A)
+    x = X.astype(np.float64)
+    g = x @ Wg[0].T.astype(np.float64)
+    ref = A + ((g / (1 + np.exp(-g))) * (x @ Wu[0].T.astype(np.float64))) @ Wd[0].T.astype(np.float64)
+    assert _rel(Y, ref) < 1e-12
+    # W_up = 0 leaves the residual untouched, bit for bit
+    Y0 = orc.expert_ffn(X, idx, alpha, Wg, np.zeros_like(Wu), Wd, A)
+    assert np.array_equal(Y0, A.astype(np.float64))
+    # W_down doubled doubles the output exactly (zero residual)
+    E, k = 6, 2
+    Wg, Wu, Wd = _layer_weights(rng, E, d, f, std=0.2)
+    idx, alpha = _random_routes(rng, T, E, k)
+    Y1 = orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, None)
+    Y2 = orc.expert_ffn(X, idx, alpha, Wg, Wu, 2 * Wd, None)
+    assert np.array_equal(Y2, 2 * Y1)
+    # relabelling the experts consistently changes nothing, bit for bit
+    perm = rng.permutation(E)
+    inv = np.argsort(perm)
+    Yp = orc.expert_ffn(X, inv[idx].astype(np.int32), alpha, Wg[perm], Wu[perm], Wd[perm], A)
+    Y = orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, A)
+    assert np.array_equal(Yp, Y)
+    # permuting the hidden units of every expert leaves y unchanged (up to rounding)
+    pf = rng.permutation(f)
+    Yf = orc.expert_ffn(X, idx, alpha, Wg[:, pf], Wu[:, pf], Wd[:, :, pf], A)
+    assert _rel(Yf, Y) < 1e-13
+
+
+def check_layer_chain(orc):
+    """The whole chain on a tiny layer equals the brute-force chain."""
+    rng = _rng(51)
+    T, d, f, E, k = 20, 64, 64, 8, 2
+    X = rng.standard_normal((T, d), dtype=np.float32)
+    Wr = rng.standard_normal((d, E), dtype=np.float32) * np.float32(0.3)
+    Wg, Wu, Wd = _layer_weights(rng, E, d, f, std=0.2)
+    A = rng.standard_normal((T, d), dtype=np.float32)
+    out = orc.layer(X, Wr, None, Wg, Wu, Wd, A, k, 0, True)
+    L = out["logits"]
+    idx_b = _lexsort_topk(L, k)
+    assert np.array_equal(out["idx"], idx_b)
+    sm = softmax(L.astype(np.float64), axis=1)
+    a = np.take_along_axis(sm, idx_b.astype(np.int64), 1)
+    a = a / a.sum(axis=1, keepdims=True)
+    ref = dense_brute_force(X, idx_b, a, Wg, Wu, Wd, A)
+    assert _rel(out["Y"], ref) < 1e-12
+    assert out["n_valid"] == T * k
+
+
+ALL_CHECKS = [check_router_golden, check_router_exact_integers, check_router_error_bound,
+              check_topk_bruteforce, check_topk_special, check_alpha, check_shared,
+              check_route_map_golden, check_route_map_bruteforce, check_route_map_errors,
+              check_ffn_dense_bruteforce, check_ffn_special, check_layer_chain]

@@ -1,0 +1,70 @@
+"""Planted-mistake test for the oracle's pins.
+
+Each case copies oracle.c, plants one plausible mistake by a text
+substitution (a dropped term, a wrong sign or index, a transposed operand,
+a reversed order, an unstable pass), builds the copy with gcc on the CPU and
+runs every pin against it. Every planted mistake must make at least one pin
+fail; otherwise the pins would not be able to tell the oracle from a wrong
+one.
+"""
+import os
+
+import pytest
+
+import oracle_pins
+from oracle import oracle as oracle_mod
+
+MUTANTS = [
+    ("router drops the bias", "if (bias) acc = acc + bias[e];", ""),
+    ("router reads W_r transposed", "Wr[i * E + e], acc", "Wr[e * d + i], acc"),
+    ("router sums in descending order", "for (int64_t i = 0; i < d; ++i)\n                acc",
+     "for (int64_t i = d - 1; i >= 0; --i)\n                acc"),
+    ("router rounds each product", "acc = fmaf(X[t * ldx + i], Wr[i * E + e], acc);",
+     "acc = acc + X[t * ldx + i] * Wr[i * E + e];"),
+    ("top-k ties go to the higher id", "l[e] > l[best]", "l[e] >= l[best]"),
+    ("renormalisation inverted", "renorm ? a / sel : a", "renorm ? a : a / sel"),
+    ("softmax denominator skips the last expert",
+     "for (int64_t e = 0; e < E; ++e) {\n            p[e] = exp",
+     "for (int64_t e = 0; e < E; ++e) {\n            if (e == E - 1) { p[e] = 0.0; continue; }\n            p[e] = exp"),
+    ("shared weight not one", "alpha[t * kp + k + s2] = 1.0;", "alpha[t * kp + k + s2] = 0.5;"),
+    ("shared id off by one", "idx[t * kp + k + s2] = (int32_t)(E + s2);",
+     "idx[t * kp + k + s2] = (int32_t)(E + s2 - 1);"),
+    ("offsets not a running sum", "offset[s + 1] = offset[s] + count[s];",
+     "offset[s + 1] = count[s];"),
+    ("cursor pass in descending route order",
+     "for (int64_t i = i0; i < i1; ++i) {\n        int32_t psi = phi[idx[i]];\n        if (psi < 0) {",
+     "for (int64_t i = i1 - 1; i >= i0; --i) {\n        int32_t psi = phi[idx[i]];\n        if (psi < 0) {"),
+    ("record stores the rank, not the token", "rec_token[p] = (int32_t)(i / kp);",
+     "rec_token[p] = (int32_t)(i % kp);"),
+    ("absent routes not marked", "route_pos[i] = -1;\n            continue;", "continue;"),
+    ("gate and up swapped", "h[n] = silu(g[n]) * u[n];", "h[n] = silu(u[n]) * g[n];"),
+    ("SiLU dropped", "h[n] = silu(g[n]) * u[n];", "h[n] = g[n] * u[n];"),
+    ("sigmoid sign flipped", "return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    ("W_down read transposed", "(double)wd[m * f + n]", "(double)wd[n * d + m]"),
+    ("residual dropped", "y[m] = A ? (double)A[t * d + m] : 0.0;", "y[m] = 0.0;"),
+    ("route weight not applied", "y[m] += alpha[i] * o;", "y[m] += o;"),
+    ("last route of each token dropped",
+     "for (int64_t j = 0; j < kp; ++j) {\n            const int64_t i = t * kp + j;",
+     "for (int64_t j = 0; j < kp - 1; ++j) {\n            const int64_t i = t * kp + j;"),
+    ("route mask ignored", "if (route_mask && !route_mask[i]) continue;", ""),
+    ("up projection reads the gate weights", "su += (double)wu[n * d + c]", "su += (double)wg[n * d + c]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    src = open(oracle_mod.SRC).read()
+    assert src.count(old) == 1, f"substitution target not unique in oracle.c: {name}"
+    mutant_src = tmp_path / "oracle_mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    oracle_mod.build(str(mutant_src), str(lib))
+    orc = oracle_mod.Oracle(str(lib))
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(orc)
+        except (AssertionError, ValueError):
+            failed.append(check.__name__)
+    assert failed, f"no pin catches the planted mistake: {name}"
+    assert os.path.exists(lib)
