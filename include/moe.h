@@ -1,0 +1,329 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed-expert MoE layer library.
+ *
+ * One sparse MoE layer's routed expert FFN over a whole prompt, as in
+ * "EStream: Fast and Memory-Efficient MoE Prefill through Expert
+ * Virtualization on Mobile NPUs" (arXiv 2609.06551):
+ *   router logits -> top-k routing (section 2.2) -> route map per physical
+ *   slot (section 3.2, Algorithm 1: slot resolve, count, prefix sum, stable
+ *   placement) -> gathered SwiGLU gate/up/down projections (Eq. 1) ->
+ *   route-weighted combine into the residual accumulator (Eq. 2),
+ * with experts held in a fixed-address slot arena (Eq. 3) that can be paged
+ * from pinned host memory (section 3.3, Eq. 4; section 3.4).
+ *
+ * Conventions
+ *  - Every pointer named "device" is GPU memory owned by the caller; the
+ *    library never frees it and never allocates device memory in a call.
+ *    "host" pointers are CPU memory owned by the caller.
+ *  - Streams are hipStream_t values passed as moe_stream (NULL = the null
+ *    stream). Every call that takes a stream only enqueues work on it and
+ *    returns without waiting for the GPU, unless stated otherwise.
+ *  - Calls return MOE_OK (0) or a negative moe_status. Arguments are checked
+ *    on the host before anything is enqueued; on error nothing is enqueued
+ *    and moe_last_error() describes the problem. Problems only the GPU can
+ *    see (an expert id outside [0, E + n_shared) in a caller-supplied top-k)
+ *    set a bit in the device error word held in the workspace; such routes
+ *    are left out, and moe_device_errors() reports and clears the word.
+ *  - Index tensors are int32, route weights and logits fp32, the output
+ *    accumulator fp32. X, the expert weights and the intermediate H use
+ *    moe_shape.dtype (bf16 or fp32).
+ *  - Route numbering: route i = t * K' + j sends token t to its rank-j
+ *    expert, K' = k + n_shared. Ranks 0..k-1 are the routed top-k in
+ *    descending logit order; ranks k..K'-1 are the shared experts
+ *    E..E+n_shared-1 with weight 1.
+ */
+#ifndef ROUTED_EXPERT_FFN_MOE_H
+#define ROUTED_EXPERT_FFN_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+typedef void *moe_stream; /* a hipStream_t */
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null pointer, bad size, bad map       */
+#define MOE_ERR_CAPACITY (-2)    /* more routes than the descriptors hold  */
+#define MOE_ERR_SLOT_STATE (-3)  /* residency protocol violated            */
+#define MOE_ERR_WORKSPACE (-4)   /* workspace missing or too small         */
+#define MOE_ERR_HIP (-5)         /* a HIP runtime call failed              */
+#define MOE_ERR_UNSUPPORTED (-6) /* shape outside what the kernels cover   */
+
+#define MOE_DT_F32 0
+#define MOE_DT_BF16 1
+
+/* Device error word bits (moe_device_errors). */
+#define MOE_DEVERR_EXPERT_ID 1 /* a top-k id outside [0, E + n_shared) */
+
+/* moe_route_build flags */
+#define MOE_ROUTE_RESET 1 /* forget which routes of the token range have been
+                             computed (implied when logits are given) */
+
+/* moe_expert_ffn flags */
+#define MOE_FFN_EXPERTS 1  /* run gate/up + SwiGLU and down for the routes */
+#define MOE_FFN_FINALIZE 2 /* combine: Y[t] += sum_j Yr[t*K' + j], fixed j order */
+#define MOE_FFN_SIMPLE_KERNEL 4 /* bf16: run the projections with the plain
+                                   LDS-tiled vector-ALU kernel instead of the
+                                   MFMA kernel (an independent second path) */
+
+/* Residency states (section 3.3, "Bounded Parameter Arena and Safe Slot Reuse") */
+#define MOE_SLOT_AVAILABLE 0
+#define MOE_SLOT_FILLING 1
+#define MOE_SLOT_READY 2
+#define MOE_SLOT_IN_USE 3
+
+#define MOE_MAX_EXPERTS 512 /* E + n_shared and P are at most this */
+
+/*
+ * Layer shape. T tokens of hidden size d, E routed experts of inner size f,
+ * top-k routing plus n_shared always-on experts, P arena slots, and a route
+ * capacity C (section 3.2: descriptors reserve capacity for at most C
+ * routes; a build may place at most C routes, larger route sets are split
+ * across invocations by token range).
+ * Limits: 1 <= k <= E <= 256, k + n_shared <= 64, E + n_shared <= 512,
+ * 1 <= P <= 512, T >= 0.
+ * bf16: d % 64 == 0, f % 64 == 0. fp32: d % 4 == 0, f % 32 == 0.
+ */
+typedef struct moe_shape {
+    int32_t T;
+    int32_t d;
+    int32_t f;
+    int32_t E;
+    int32_t k;
+    int32_t n_shared;
+    int32_t P;
+    int32_t capacity; /* C, >= 1 */
+    int32_t dtype;    /* MOE_DT_BF16 or MOE_DT_F32 */
+    int32_t renorm;   /* 1: top-k weights renormalised over the k selected */
+    int64_t ldx;      /* row stride of X in elements, >= d */
+    int64_t ldy;      /* row stride of Y in elements, >= d, multiple of 4 */
+} moe_shape;
+
+/*
+ * Route descriptors (section 3.2, "Composed Sparse Route and Parameter
+ * Binding"; the compressed-sparse-row route map). All device, caller-owned.
+ *   topk_idx    [T][K'] int32  expert ids by rank (written from logits, or
+ *                              supplied by the caller)
+ *   topk_w      [T][K'] fp32   route weights alpha
+ *   slot_count  [P]     int32  routes placed in each slot by the last build
+ *   slot_offset [P+1]   int32  exclusive prefix sum of slot_count;
+ *                              slot_offset[P] = n_valid
+ *   rec_token   [C]     int32  token of record p (records of slot s occupy
+ *                              [slot_offset[s], slot_offset[s+1]), in
+ *                              ascending route order)
+ *   rec_route   [C]     int32  route index i of record p
+ *   route_pos   [T*K']  int32  record position of route i in the last build
+ *                              that covered it, -1 if it was left out
+ */
+typedef struct moe_routes {
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *slot_count;
+    int32_t *slot_offset;
+    int32_t *rec_token;
+    int32_t *rec_route;
+    int32_t *route_pos;
+} moe_routes;
+
+/* Opaque host handle of the slot arena and its residency table. */
+typedef struct moe_arena moe_arena;
+
+/* Library version string. */
+const char *moe_version(void);
+
+/* Copy the calling thread's last error message into buf (NUL-terminated,
+ * truncated to n bytes) and return the status of that error (MOE_OK if none). */
+moe_status moe_last_error(char *buf, size_t n);
+
+/*
+ * Bytes of device workspace the calls need for this shape. The workspace
+ * holds the device error word, per-block route counts and ranks, the router
+ * logits, the SwiGLU intermediate H [C][f] and the per-route fp32 output rows
+ * Yr [T*K'][d], plus the per-route "computed" marks. One workspace belongs to
+ * one layer invocation at a time; it must persist from moe_route_build to
+ * the finalizing moe_expert_ffn. Returns 0 for an invalid shape.
+ */
+size_t moe_workspace_bytes(const moe_shape *shape);
+
+/*
+ * Prepare a freshly allocated workspace: clears the device error word (no
+ * other region needs initial contents). Call once after allocating `ws`;
+ * enqueued on `stream`.
+ */
+moe_status moe_workspace_init(const moe_shape *shape, void *ws, size_t ws_bytes,
+                              moe_stream stream);
+
+/*
+ * Synchronize `stream`, read the device error word of `ws`, store it in
+ * *errors (may be NULL) and clear it. Returns MOE_OK, or MOE_ERR_INVALID_ARG
+ * if bits were set.
+ */
+moe_status moe_device_errors(const moe_shape *shape, void *ws, size_t ws_bytes,
+                             int32_t *errors, moe_stream stream);
+
+/*
+ * Router logits, the input of top-k routing (section 2.2).
+ *   X      device [T][ldx] dtype
+ *   W_r    device [d][E] fp32
+ *   bias   device [E] fp32 or NULL (added after the product)
+ *   logits device [T][E] fp32, output
+ * logits[t][e] = acc + bias[e], where acc is the fp32 fused multiply-add
+ * chain over i = 0..d-1 in ascending order starting from 0: this fixes the
+ * bits of every logit, so the top-k decision is reproducible.
+ */
+moe_status moe_router_logits(const moe_shape *shape, const void *X,
+                             const float *W_r, const float *bias,
+                             float *logits, moe_stream stream);
+
+/*
+ * Route build for the tokens t0 .. t0+nt-1 (section 3.2, Algorithm 1).
+ *   logits  device [T][E] fp32 or NULL. When given, top-k routing runs first
+ *           for the token range: ranks by descending logit, equal logits to
+ *           the lower expert id (NaN is taken as -infinity); alpha is the
+ *           softmax over all E of the selected logits, renormalised over the
+ *           k when shape->renorm; shared ranks appended. Results go to
+ *           routes->topk_idx / topk_w. When NULL, those arrays must already
+ *           hold the routing (written by the caller or an earlier build).
+ *   phi     host [E + n_shared] int32, the placement map: phi[e] = slot of
+ *           expert e in [0, P), or -1 if not resident; no two experts may
+ *           share a slot. Routes of absent experts are left out.
+ *   flags   MOE_ROUTE_RESET or 0.
+ *   routes  descriptors, see moe_routes. slot_count, slot_offset, rec_* are
+ *           rewritten for this build; route_pos is written for the range.
+ *   ws      device workspace of at least moe_workspace_bytes(shape) bytes.
+ * Requires nt * K' <= capacity (MOE_ERR_CAPACITY otherwise) and
+ * 0 <= t0 <= t0 + nt <= T. Records are stable: within a slot they are in
+ * ascending route order. Everything is bit-exact and run-to-run identical.
+ */
+moe_status moe_route_build(const moe_shape *shape, int32_t t0, int32_t nt,
+                           const float *logits, const int32_t *phi,
+                           int32_t flags, const moe_routes *routes, void *ws,
+                           size_t ws_bytes, moe_stream stream);
+
+/*
+ * Expert FFN over the routes of the last build, then (optionally) the
+ * combine (Eq. 1-2; section 3.2 "Fused Expert Execution").
+ *   X      device [T][ldx] dtype, the source activations (gathered by
+ *          rec_token)
+ *   Y      device [T][ldy] fp32; holds the residual A on entry and
+ *          A + sum_j alpha_tj F_e(X_t) after a MOE_FFN_FINALIZE call
+ *   arena  slot arena holding the experts named by phi
+ *   phi    host [E + n_shared], the same map given to the build. Every slot
+ *          it names must hold that expert and be Ready or In-use in the arena
+ *          (MOE_ERR_SLOT_STATE otherwise); the stream waits for each such
+ *          slot's load, and each slot's release is recorded after the work.
+ *   flags  MOE_FFN_EXPERTS and/or MOE_FFN_FINALIZE (and optionally
+ *          MOE_FFN_SIMPLE_KERNEL).
+ * MOE_FFN_EXPERTS: for each record p of slot s, H[p] = SiLU(g) * u with
+ * (g, u) = X[rec_token[p]] times slot s's gate/up slice, then
+ * Yr[rec_route[p]] = alpha * (H[p] times slot s's down slice); the route is
+ * marked computed. MOE_FFN_FINALIZE: for every token, Y[t] += Yr[t*K'+j] for
+ * j = 0..K'-1 in ascending order over the computed routes. The sum order is
+ * fixed, so Y is bitwise run-to-run identical and independent of phi and P.
+ * arena and phi may be NULL when only MOE_FFN_FINALIZE is set.
+ */
+moe_status moe_expert_ffn(const moe_shape *shape, const void *X, float *Y,
+                          const moe_routes *routes, moe_arena *arena,
+                          const int32_t *phi, int32_t flags, void *ws,
+                          size_t ws_bytes, moe_stream stream);
+
+/*
+ * Whole layer: router (when W_r is given; else logits must be given),
+ * route build, expert FFN and combine.
+ *   X, W_r, bias, logits, Y, routes, ws: as above (W_r/bias or logits).
+ *   host_gu, host_d: NULL for a resident layer -- every expert must then be
+ *     Ready in the arena. Otherwise arrays of E + n_shared host pointers to
+ *     each expert's prepacked gate/up and down slices in pinned memory: the
+ *     experts are paged through the arena's banks of G slots on the copy
+ *     stream, group by group, overlapped with compute (section 3.4), and
+ *     groups with no routes are skipped. Paging synchronizes the compute
+ *     stream once, after routing, to read the per-expert route counts.
+ * Token ranges are split so that each build fits the capacity.
+ */
+moe_status moe_layer_prefill(const moe_shape *shape, const void *X,
+                             const float *W_r, const float *bias,
+                             const float *logits, float *Y, moe_arena *arena,
+                             const void *const *host_gu,
+                             const void *const *host_d,
+                             const moe_routes *routes, void *ws,
+                             size_t ws_bytes, moe_stream compute,
+                             moe_stream copy);
+
+/*
+ * Gate/up packing (section 3.3, "Offline NPU-Consumable Weight Layout":
+ * experts are stored in the layout the kernels consume). One expert's gate
+ * W_g [f][d] and up W_u [f][d] become one [2f][d] slice whose rows alternate
+ * in blocks of 32: rows 64q..64q+31 are gate rows 32q..32q+31 and rows
+ * 64q+32..64q+63 are up rows 32q..32q+31. The down slice is W_d [d][f]
+ * unchanged.
+ * moe_pack_gate_up: device, n experts, source expert stride src_stride and
+ * destination stride dst_stride (elements).
+ * moe_pack_gate_up_host: the same on host memory, synchronous.
+ */
+moe_status moe_pack_gate_up(const moe_shape *shape, const void *W_g,
+                            const void *W_u, void *dst, int32_t n,
+                            int64_t src_stride, int64_t dst_stride,
+                            moe_stream stream);
+moe_status moe_pack_gate_up_host(const moe_shape *shape, const void *W_g,
+                                 const void *W_u, void *dst);
+
+/*
+ * Slot arena (Eq. 3: the slice j of slot s starts at plane_j + s * S_j).
+ *   plane_gu  device, P slots of [2f][d] dtype, slot stride stride_gu
+ *   plane_d   device, P slots of [d][f] dtype, slot stride stride_d
+ *   G         slots per bank (1 <= G <= P, P % G == 0); banks are used when
+ *             paging (Eq. 4: phi(e) = b*G + r(e))
+ * Creates the residency table with every slot Available.
+ */
+moe_status moe_arena_create(moe_arena **out, const moe_shape *shape,
+                            void *plane_gu, void *plane_d, int64_t stride_gu,
+                            int64_t stride_d, int32_t G);
+void moe_arena_destroy(moe_arena *arena);
+
+/*
+ * Load expert `expert` into `slot`: Available/Ready/In-use -> Filling ->
+ * Ready. src_gu ([2f][d], packed) and src_d ([d][f]) are host (pinned) or
+ * device pointers; the copies run on copy_stream after the slot's previous
+ * release (if any), and the slot's ready event is recorded after them. The
+ * slot's previous mapping is withdrawn first. MOE_ERR_SLOT_STATE if the
+ * expert is mapped to another slot or the slot is Filling.
+ */
+moe_status arena_bind_slot(moe_arena *arena, int32_t slot, int32_t expert,
+                           const void *src_gu, const void *src_d,
+                           moe_stream copy_stream);
+
+/* Publish a slot whose contents the caller has written by other means
+ * (e.g. moe_pack_gate_up into the plane) as holding `expert`; the ready
+ * event is recorded on `stream` after that work. */
+moe_status arena_publish_slot(moe_arena *arena, int32_t slot, int32_t expert,
+                              moe_stream stream);
+
+/* Withdraw a slot's mapping (Ready or In-use -> Available). A later bind of
+ * the slot still waits for its last release. */
+moe_status arena_release_slot(moe_arena *arena, int32_t slot);
+
+/* The current placement map over Ready and In-use slots: phi[e] = slot or
+ * -1, for e < n (n >= E + n_shared). */
+moe_status arena_phi(const moe_arena *arena, int32_t *phi, int32_t n);
+
+/* State (MOE_SLOT_*) and owner expert (-1 if none) of one slot. */
+moe_status arena_slot_info(const moe_arena *arena, int32_t slot,
+                           int32_t *state, int32_t *expert);
+
+/*
+ * Diagnostics: run one v_mfma_f32_32x32x16_bf16 on integer-valued operands
+ * laid out as the expert kernels assume and write the 32x32 product, row
+ * major, to out (device, 1024 floats). The product equals A*B (A[i][k] =
+ * (3i + 5k) % 7 - 3, B[k][j] = (2k + 7j) % 5 - 2) exactly iff the kernels'
+ * lane layout is the hardware's.
+ */
+moe_status moe_selftest_mfma_layout(float *out, moe_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ROUTED_EXPERT_FFN_MOE_H */

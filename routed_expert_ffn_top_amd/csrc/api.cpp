@@ -1,0 +1,676 @@
+// C ABI of the routed-expert MoE layer library: argument checks, the slot
+// arena with its residency table, and the order of kernel launches.
+//
+// Residency table (EStream, section 3.3, "Bounded Parameter Arena and Safe
+// Slot Reuse"): a slot is Available, Filling (owner recorded, mapping hidden),
+// Ready (published) or In-use (submitted). On a GPU stream the protocol is
+// carried by two events per slot: "ready" is recorded on the copy stream
+// after the slot's slices are copied, and every invocation that reads the
+// slot waits for it; "release" is recorded on the compute stream after the
+// last invocation that reads the slot, and a later load into the slot waits
+// for it. So no invocation sees a partly loaded expert, and no load
+// overwrites a slot that queued work still reads, without any host wait.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local moe_status g_status = MOE_OK;
+thread_local char g_msg[512] = {0};
+
+moe_status fail(moe_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+    va_end(ap);
+    g_status = st;
+    return st;
+}
+
+moe_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                        \
+    do {                                           \
+        hipError_t _e = (expr);                    \
+        if (_e != hipSuccess) return hip_fail(_e, what); \
+    } while (0)
+
+#define MOE_TRY(expr)                  \
+    do {                               \
+        moe_status _s = (expr);        \
+        if (_s != MOE_OK) return _s;   \
+    } while (0)
+
+inline hipStream_t S(moe_stream s) { return (hipStream_t)s; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_shape(const moe_shape *s)
+{
+    if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+    if (s->T < 0 || s->d <= 0 || s->f <= 0)
+        return fail(MOE_ERR_INVALID_ARG, "bad sizes T=%d d=%d f=%d", s->T, s->d, s->f);
+    if (s->E < 1 || s->E > 256 || s->k < 1 || s->k > s->E)
+        return fail(MOE_ERR_INVALID_ARG, "need 1 <= k <= E <= 256 (E=%d k=%d)", s->E, s->k);
+    if (s->n_shared < 0 || s->E + s->n_shared > kMaxExp)
+        return fail(MOE_ERR_INVALID_ARG, "E + n_shared must be <= %d", kMaxExp);
+    if (s->k + s->n_shared > 64) return fail(MOE_ERR_UNSUPPORTED, "k + n_shared must be <= 64");
+    if (s->P < 1 || s->P > kMaxExp) return fail(MOE_ERR_INVALID_ARG, "need 1 <= P <= %d", kMaxExp);
+    if (s->capacity < 1) return fail(MOE_ERR_INVALID_ARG, "capacity must be >= 1");
+    if (s->dtype != MOE_DT_BF16 && s->dtype != MOE_DT_F32)
+        return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_DT_BF16 or MOE_DT_F32");
+    if (s->ldx < s->d || s->ldy < s->d || (s->ldy % 4) != 0)
+        return fail(MOE_ERR_INVALID_ARG, "need ldx >= d, ldy >= d, ldy %% 4 == 0");
+    if ((s->d % 4) != 0) return fail(MOE_ERR_UNSUPPORTED, "d must be a multiple of 4");
+    if (s->dtype == MOE_DT_BF16) {
+        if ((s->d % 64) != 0 || (s->f % 64) != 0)
+            return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need d %% 64 == 0 and f %% 64 == 0");
+        if ((s->ldx % 8) != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 X needs ldx %% 8 == 0");
+    } else if ((s->f % 32) != 0) {
+        return fail(MOE_ERR_UNSUPPORTED, "fp32 layers need f %% 32 == 0");
+    }
+    const int64_t routes = (int64_t)s->T * (s->k + s->n_shared);
+    if (routes > INT32_MAX / 2 || (int64_t)s->capacity * s->f > (int64_t)1 << 40)
+        return fail(MOE_ERR_UNSUPPORTED, "too many routes");
+    return MOE_OK;
+}
+
+moe_status check_ws(const moe_shape *s, void *ws, size_t ws_bytes, WsLayout *w)
+{
+    *w = ws_layout(*s);
+    if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(ws, 256)) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < w->total)
+        return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, w->total);
+    return MOE_OK;
+}
+
+moe_status check_routes(const moe_routes *r)
+{
+    if (!r || !r->topk_idx || !r->topk_w || !r->slot_count || !r->slot_offset || !r->rec_token ||
+        !r->rec_route || !r->route_pos)
+        return fail(MOE_ERR_INVALID_ARG, "route descriptor pointer is NULL");
+    return MOE_OK;
+}
+
+moe_status check_phi(const moe_shape *s, const int32_t *phi, PhiArg *out)
+{
+    if (!phi) return fail(MOE_ERR_INVALID_ARG, "phi is NULL");
+    const int ne = s->E + s->n_shared;
+    std::vector<int> used(s->P, -1);
+    for (int e = 0; e < ne; ++e) {
+        const int v = phi[e];
+        if (v < -1 || v >= s->P) return fail(MOE_ERR_INVALID_ARG, "phi[%d] = %d outside [-1, P)", e, v);
+        if (v >= 0) {
+            if (used[v] >= 0)
+                return fail(MOE_ERR_INVALID_ARG, "phi maps experts %d and %d to slot %d", used[v], e, v);
+            used[v] = e;
+        }
+        out->v[e] = v;
+    }
+    for (int e = ne; e < kMaxExp; ++e) out->v[e] = -1;
+    return MOE_OK;
+}
+
+template <typename T>
+T *ws_at(void *ws, size_t off) { return (T *)((char *)ws + off); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// arena
+
+struct moe_arena {
+    std::mutex mu;
+    moe_shape shape;
+    char *plane_gu;
+    char *plane_d;
+    int64_t stride_gu, stride_d;  // elements
+    int G;
+    int esz;
+    std::vector<int> state, owner, slot_of;  // per slot, per slot, per expert
+    // "ready": one event per slot, recorded after the slot's load; a stream
+    // that already waited for the current record does not wait again.
+    std::vector<hipEvent_t> ready;
+    std::vector<uint64_t> ready_gen;
+    std::vector<hipStream_t> waited_stream;
+    std::vector<uint64_t> waited_gen;
+    // "release": each invocation records one event from a ring of kRing on its
+    // stream after its work; a slot remembers the ring entry of its last use,
+    // and a later load into the slot waits for it. Before a ring entry is
+    // recorded again its previous record is waited for on the host (it is
+    // kRing invocations old) and the slots that pointed at it are cleared.
+    static constexpr int kRing = 32;
+    std::vector<hipEvent_t> ring;
+    int ring_pos = 0;
+    std::vector<int> last_use;  // per slot: ring index or -1
+};
+
+namespace {
+
+moe_status arena_events(moe_arena *a, int slot)
+{
+    if (!a->ready[slot]) HIP_TRY(hipEventCreateWithFlags(&a->ready[slot], hipEventDisableTiming), "hipEventCreate");
+    return MOE_OK;
+}
+
+// Available/Ready/In-use -> Filling for (slot, expert); caller holds the lock.
+moe_status arena_reserve(moe_arena *a, int slot, int expert)
+{
+    const int ne = a->shape.E + a->shape.n_shared;
+    if (slot < 0 || slot >= a->shape.P) return fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, P)", slot);
+    if (expert < 0 || expert >= ne) return fail(MOE_ERR_INVALID_ARG, "expert %d outside [0, %d)", expert, ne);
+    if (a->state[slot] == MOE_SLOT_FILLING) return fail(MOE_ERR_SLOT_STATE, "slot %d is Filling", slot);
+    if (a->slot_of[expert] >= 0 && a->slot_of[expert] != slot)
+        return fail(MOE_ERR_SLOT_STATE, "expert %d already occupies slot %d", expert, a->slot_of[expert]);
+    if (a->owner[slot] >= 0) a->slot_of[a->owner[slot]] = -1;  // withdraw the old mapping
+    a->owner[slot] = expert;
+    a->slot_of[expert] = -1;  // hidden while Filling
+    a->state[slot] = MOE_SLOT_FILLING;
+    return MOE_OK;
+}
+
+void arena_publish_locked(moe_arena *a, int slot)
+{
+    a->state[slot] = MOE_SLOT_READY;
+    a->slot_of[a->owner[slot]] = slot;
+}
+
+void arena_abort_fill(moe_arena *a, int slot)
+{
+    a->owner[slot] = -1;
+    a->state[slot] = MOE_SLOT_AVAILABLE;
+}
+
+moe_status arena_bind_locked(moe_arena *a, int slot, int expert, const void *src_gu, const void *src_d,
+                             hipStream_t st)
+{
+    if (!src_gu || !src_d) return fail(MOE_ERR_INVALID_ARG, "bind source is NULL");
+    MOE_TRY(arena_reserve(a, slot, expert));
+    moe_status rc = arena_events(a, slot);
+    const moe_shape &s = a->shape;
+    const size_t gu_bytes = (size_t)2 * s.f * s.d * a->esz, d_bytes = (size_t)s.d * s.f * a->esz;
+    hipError_t e = hipSuccess;
+    if (rc == MOE_OK && a->last_use[slot] >= 0) e = hipStreamWaitEvent(st, a->ring[a->last_use[slot]], 0);
+    if (rc == MOE_OK && e == hipSuccess)
+        e = hipMemcpyAsync(a->plane_gu + (size_t)slot * a->stride_gu * a->esz, src_gu, gu_bytes,
+                           hipMemcpyDefault, st);
+    if (rc == MOE_OK && e == hipSuccess)
+        e = hipMemcpyAsync(a->plane_d + (size_t)slot * a->stride_d * a->esz, src_d, d_bytes,
+                           hipMemcpyDefault, st);
+    if (rc == MOE_OK && e == hipSuccess) e = hipEventRecord(a->ready[slot], st);
+    if (rc != MOE_OK || e != hipSuccess) {
+        arena_abort_fill(a, slot);
+        return rc != MOE_OK ? rc : hip_fail(e, "arena_bind_slot");
+    }
+    a->ready_gen[slot] += 1;
+    arena_publish_locked(a, slot);
+    return MOE_OK;
+}
+
+// Checks phi against the arena, makes `st` wait for each named slot's load.
+moe_status arena_acquire(moe_arena *a, const int32_t *phi, hipStream_t st)
+{
+    const int ne = a->shape.E + a->shape.n_shared;
+    for (int e = 0; e < ne; ++e) {
+        const int s = phi[e];
+        if (s < 0) continue;
+        if ((a->state[s] != MOE_SLOT_READY && a->state[s] != MOE_SLOT_IN_USE) || a->owner[s] != e)
+            return fail(MOE_ERR_SLOT_STATE, "phi maps expert %d to slot %d, which is not Ready with it", e, s);
+    }
+    for (int e = 0; e < ne; ++e) {
+        const int s = phi[e];
+        if (s < 0 || (a->waited_stream[s] == st && a->waited_gen[s] == a->ready_gen[s])) continue;
+        HIP_TRY(hipStreamWaitEvent(st, a->ready[s], 0), "hipStreamWaitEvent");
+        a->waited_stream[s] = st;
+        a->waited_gen[s] = a->ready_gen[s];
+    }
+    return MOE_OK;
+}
+
+moe_status arena_release_after(moe_arena *a, const int32_t *phi, hipStream_t st)
+{
+    const int ne = a->shape.E + a->shape.n_shared;
+    const int pos = a->ring_pos;
+    if (!a->ring[pos]) {
+        HIP_TRY(hipEventCreateWithFlags(&a->ring[pos], hipEventDisableTiming), "hipEventCreate");
+    } else {
+        HIP_TRY(hipEventSynchronize(a->ring[pos]), "hipEventSynchronize");
+        for (int s = 0; s < a->shape.P; ++s)
+            if (a->last_use[s] == pos) a->last_use[s] = -1;
+    }
+    HIP_TRY(hipEventRecord(a->ring[pos], st), "hipEventRecord");
+    a->ring_pos = (pos + 1) % moe_arena::kRing;
+    for (int e = 0; e < ne; ++e) {
+        const int s = phi[e];
+        if (s < 0) continue;
+        a->last_use[s] = pos;
+        a->state[s] = MOE_SLOT_IN_USE;
+    }
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// internal steps (arguments already checked)
+
+moe_status route_build_impl(const moe_shape &s, const WsLayout &w, int t0, int nt, const float *logits,
+                            const PhiArg &phi, int flags, const moe_routes &r, void *ws, hipStream_t st)
+{
+    const int kp = s.k + s.n_shared;
+    int32_t *done = ws_at<int32_t>(ws, w.done);
+    int reset = (flags & MOE_ROUTE_RESET) ? 1 : 0;
+    if (logits) {
+        HIP_TRY(launch_topk(s, t0, nt, logits, r.topk_idx, r.topk_w, done, st), "top-k launch");
+        reset = 0;  // top-k cleared the marks of the range
+    }
+    const int64_t i0 = (int64_t)t0 * kp, n = (int64_t)nt * kp;
+    const int nblk = (int)((n + kRouteBlock - 1) / kRouteBlock);
+    int32_t *blk = ws_at<int32_t>(ws, w.blk);
+    int32_t *rank = ws_at<int32_t>(ws, w.rank);
+    int32_t *err = ws_at<int32_t>(ws, w.err);
+    HIP_TRY(launch_route_count(s, i0, n, r.topk_idx, phi, blk, rank, err, done, reset, st), "route count launch");
+    HIP_TRY(launch_route_scan(s, nblk, blk, r.slot_count, r.slot_offset, st), "route scan launch");
+    HIP_TRY(launch_route_place(s, i0, n, r.topk_idx, phi, blk, rank, r.rec_token, r.rec_route, r.route_pos, st),
+            "route place launch");
+    return MOE_OK;
+}
+
+GemmArgs gemm_args(const moe_shape &s, const moe_routes &r, const moe_arena *a)
+{
+    GemmArgs g{};
+    g.slot_offset = r.slot_offset;
+    g.P = s.P;
+    g.rec_token = r.rec_token;
+    g.rec_route = r.rec_route;
+    g.topk_w = r.topk_w;
+    (void)a;
+    return g;
+}
+
+moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, const moe_routes &r,
+                        moe_arena *a, int max_rows, bool simple, void *ws, hipStream_t st)
+{
+    GemmArgs g = gemm_args(s, r, a);
+    g.A = X;
+    g.lda = s.ldx;
+    g.B = a->plane_gu;
+    g.slot_stride = a->stride_gu;
+    g.N = 2 * s.f;
+    g.K = s.d;
+    g.C = ws_at<char>(ws, w.H);
+    g.ldc = s.f;
+    HIP_TRY(launch_gate_up(s, g, max_rows, simple, st), "gate/up launch");
+    GemmArgs h = gemm_args(s, r, a);
+    h.A = ws_at<char>(ws, w.H);
+    h.lda = s.f;
+    h.B = a->plane_d;
+    h.slot_stride = a->stride_d;
+    h.N = s.d;
+    h.K = s.f;
+    h.C = ws_at<float>(ws, w.Yr);
+    h.ldc = s.d;
+    h.done = ws_at<int32_t>(ws, w.done);
+    HIP_TRY(launch_down(s, h, max_rows, simple, st), "down launch");
+    return MOE_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+
+extern "C" {
+
+const char *moe_version(void) { return "routed-expert-ffn-gfx950 0.1"; }
+
+moe_status moe_last_error(char *buf, size_t n)
+{
+    if (buf && n) {
+        strncpy(buf, g_msg, n - 1);
+        buf[n - 1] = 0;
+    }
+    return g_status;
+}
+
+size_t moe_workspace_bytes(const moe_shape *shape)
+{
+    if (check_shape(shape) != MOE_OK) return 0;
+    return ws_layout(*shape).total;
+}
+
+moe_status moe_workspace_init(const moe_shape *shape, void *ws, size_t ws_bytes, moe_stream stream)
+{
+    MOE_TRY(check_shape(shape));
+    WsLayout w;
+    MOE_TRY(check_ws(shape, ws, ws_bytes, &w));
+    HIP_TRY(launch_fill_i32(ws_at<int32_t>(ws, w.err), 0, 64, S(stream)), "fill launch");
+    return MOE_OK;
+}
+
+moe_status moe_device_errors(const moe_shape *shape, void *ws, size_t ws_bytes, int32_t *errors,
+                             moe_stream stream)
+{
+    MOE_TRY(check_shape(shape));
+    WsLayout w;
+    MOE_TRY(check_ws(shape, ws, ws_bytes, &w));
+    int32_t v = 0;
+    HIP_TRY(hipStreamSynchronize(S(stream)), "hipStreamSynchronize");
+    HIP_TRY(hipMemcpy(&v, ws_at<int32_t>(ws, w.err), 4, hipMemcpyDeviceToHost), "hipMemcpy");
+    if (v) HIP_TRY(hipMemset(ws_at<int32_t>(ws, w.err), 0, 4), "hipMemset");
+    if (errors) *errors = v;
+    if (v) return fail(MOE_ERR_INVALID_ARG, "device error word 0x%x (bit 0: expert id out of range)", v);
+    return MOE_OK;
+}
+
+moe_status moe_router_logits(const moe_shape *shape, const void *X, const float *W_r, const float *bias,
+                             float *logits, moe_stream stream)
+{
+    MOE_TRY(check_shape(shape));
+    if (!X || !W_r || !logits) return fail(MOE_ERR_INVALID_ARG, "router: NULL pointer");
+    HIP_TRY(launch_router_logits(*shape, X, W_r, bias, logits, S(stream)), "router launch");
+    return MOE_OK;
+}
+
+moe_status moe_route_build(const moe_shape *shape, int32_t t0, int32_t nt, const float *logits,
+                           const int32_t *phi, int32_t flags, const moe_routes *routes, void *ws,
+                           size_t ws_bytes, moe_stream stream)
+{
+    MOE_TRY(check_shape(shape));
+    if (shape->T == 0) return MOE_OK;  // an empty prompt: nothing to do
+    MOE_TRY(check_routes(routes));
+    WsLayout w;
+    MOE_TRY(check_ws(shape, ws, ws_bytes, &w));
+    if (t0 < 0 || nt < 0 || (int64_t)t0 + nt > shape->T)
+        return fail(MOE_ERR_INVALID_ARG, "token range [%d, %d) outside [0, %d)", t0, t0 + nt, shape->T);
+    const int64_t kp = shape->k + shape->n_shared;
+    if ((int64_t)nt * kp > shape->capacity)
+        return fail(MOE_ERR_CAPACITY, "%lld routes exceed capacity %d", (long long)nt * kp, shape->capacity);
+    PhiArg pa;
+    MOE_TRY(check_phi(shape, phi, &pa));
+    return route_build_impl(*shape, w, t0, nt, logits, pa, flags, *routes, ws, S(stream));
+}
+
+moe_status moe_expert_ffn(const moe_shape *shape, const void *X, float *Y, const moe_routes *routes,
+                          moe_arena *arena, const int32_t *phi, int32_t flags, void *ws, size_t ws_bytes,
+                          moe_stream stream)
+{
+    MOE_TRY(check_shape(shape));
+    if (shape->T == 0) return MOE_OK;  // an empty prompt: nothing to do
+    MOE_TRY(check_routes(routes));
+    WsLayout w;
+    MOE_TRY(check_ws(shape, ws, ws_bytes, &w));
+    if (flags & MOE_FFN_EXPERTS) {
+        if (!X || !arena || !phi) return fail(MOE_ERR_INVALID_ARG, "expert FFN: X, arena and phi are required");
+        if (arena->shape.d != shape->d || arena->shape.f != shape->f || arena->shape.P != shape->P ||
+            arena->shape.dtype != shape->dtype || arena->shape.E != shape->E ||
+            arena->shape.n_shared != shape->n_shared)
+            return fail(MOE_ERR_INVALID_ARG, "arena was made for another shape");
+        if (shape->dtype == MOE_DT_BF16 && !aligned(X, 16))
+            return fail(MOE_ERR_INVALID_ARG, "X must be 16-byte aligned");
+        PhiArg pa;
+        MOE_TRY(check_phi(shape, phi, &pa));
+        std::lock_guard<std::mutex> lk(arena->mu);
+        MOE_TRY(arena_acquire(arena, phi, S(stream)));
+        const int max_rows = std::min<int64_t>(shape->capacity, (int64_t)shape->T * (shape->k + shape->n_shared));
+        MOE_TRY(experts_impl(*shape, w, X, *routes, arena, max_rows, (flags & MOE_FFN_SIMPLE_KERNEL) != 0, ws,
+                             S(stream)));
+        MOE_TRY(arena_release_after(arena, phi, S(stream)));
+    }
+    if (flags & MOE_FFN_FINALIZE) {
+        if (!Y || !aligned(Y, 16)) return fail(MOE_ERR_INVALID_ARG, "Y must be non-NULL and 16-byte aligned");
+        HIP_TRY(launch_combine(*shape, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), S(stream)),
+                "combine launch");
+    }
+    return MOE_OK;
+}
+
+moe_status moe_pack_gate_up(const moe_shape *shape, const void *W_g, const void *W_u, void *dst, int32_t n,
+                            int64_t src_stride, int64_t dst_stride, moe_stream stream)
+{
+    MOE_TRY(check_shape(shape));
+    if (!W_g || !W_u || !dst || n < 0) return fail(MOE_ERR_INVALID_ARG, "pack: bad arguments");
+    const int64_t fd = (int64_t)shape->f * shape->d;
+    if (n > 1 && (src_stride < fd || dst_stride < 2 * fd))
+        return fail(MOE_ERR_INVALID_ARG, "pack: strides smaller than a slice");
+    HIP_TRY(launch_pack_gate_up(*shape, W_g, W_u, dst, n, src_stride, dst_stride, S(stream)), "pack launch");
+    return MOE_OK;
+}
+
+moe_status moe_pack_gate_up_host(const moe_shape *shape, const void *W_g, const void *W_u, void *dst)
+{
+    MOE_TRY(check_shape(shape));
+    if (!W_g || !W_u || !dst) return fail(MOE_ERR_INVALID_ARG, "pack: NULL pointer");
+    const size_t esz = shape->dtype == MOE_DT_BF16 ? 2 : 4;
+    const size_t row = (size_t)shape->d * esz;
+    for (int r = 0; r < 2 * shape->f; ++r) {
+        const int q = r / 64, w = r % 64;
+        const char *src = w < 32 ? (const char *)W_g + (size_t)(32 * q + w) * row
+                                 : (const char *)W_u + (size_t)(32 * q + w - 32) * row;
+        memcpy((char *)dst + (size_t)r * row, src, row);
+    }
+    return MOE_OK;
+}
+
+moe_status moe_arena_create(moe_arena **out, const moe_shape *shape, void *plane_gu, void *plane_d,
+                            int64_t stride_gu, int64_t stride_d, int32_t G)
+{
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    MOE_TRY(check_shape(shape));
+    if (!plane_gu || !plane_d) return fail(MOE_ERR_INVALID_ARG, "plane is NULL");
+    const int64_t fd = (int64_t)shape->f * shape->d;
+    if (stride_gu < 2 * fd || stride_d < fd)
+        return fail(MOE_ERR_INVALID_ARG, "slot strides smaller than the slices");
+    if (G < 1 || G > shape->P || shape->P % G != 0)
+        return fail(MOE_ERR_INVALID_ARG, "need 1 <= G <= P and P %% G == 0");
+    const int esz = shape->dtype == MOE_DT_BF16 ? 2 : 4;
+    if (!aligned(plane_gu, 16) || !aligned(plane_d, 16) || (stride_gu * esz) % 16 || (stride_d * esz) % 16)
+        return fail(MOE_ERR_INVALID_ARG, "planes and slot strides must be 16-byte aligned");
+    moe_arena *a = new moe_arena();
+    a->shape = *shape;
+    a->plane_gu = (char *)plane_gu;
+    a->plane_d = (char *)plane_d;
+    a->stride_gu = stride_gu;
+    a->stride_d = stride_d;
+    a->G = G;
+    a->esz = esz;
+    a->state.assign(shape->P, MOE_SLOT_AVAILABLE);
+    a->owner.assign(shape->P, -1);
+    a->slot_of.assign(shape->E + shape->n_shared, -1);
+    a->ready.assign(shape->P, nullptr);
+    a->ready_gen.assign(shape->P, 0);
+    a->waited_stream.assign(shape->P, nullptr);
+    a->waited_gen.assign(shape->P, 0);
+    a->ring.assign(moe_arena::kRing, nullptr);
+    a->last_use.assign(shape->P, -1);
+    *out = a;
+    return MOE_OK;
+}
+
+void moe_arena_destroy(moe_arena *a)
+{
+    if (!a) return;
+    for (auto e : a->ready)
+        if (e) (void)hipEventDestroy(e);
+    for (auto e : a->ring)
+        if (e) (void)hipEventDestroy(e);
+    delete a;
+}
+
+moe_status arena_bind_slot(moe_arena *a, int32_t slot, int32_t expert, const void *src_gu, const void *src_d,
+                           moe_stream copy_stream)
+{
+    if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
+    std::lock_guard<std::mutex> lk(a->mu);
+    return arena_bind_locked(a, slot, expert, src_gu, src_d, S(copy_stream));
+}
+
+moe_status arena_publish_slot(moe_arena *a, int32_t slot, int32_t expert, moe_stream stream)
+{
+    if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
+    std::lock_guard<std::mutex> lk(a->mu);
+    MOE_TRY(arena_reserve(a, slot, expert));
+    moe_status rc = arena_events(a, slot);
+    hipError_t e = rc == MOE_OK ? hipEventRecord(a->ready[slot], S(stream)) : hipSuccess;
+    if (rc != MOE_OK || e != hipSuccess) {
+        arena_abort_fill(a, slot);
+        return rc != MOE_OK ? rc : hip_fail(e, "arena_publish_slot");
+    }
+    a->ready_gen[slot] += 1;
+    arena_publish_locked(a, slot);
+    return MOE_OK;
+}
+
+moe_status arena_release_slot(moe_arena *a, int32_t slot)
+{
+    if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
+    std::lock_guard<std::mutex> lk(a->mu);
+    if (slot < 0 || slot >= a->shape.P) return fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, P)", slot);
+    if (a->state[slot] == MOE_SLOT_FILLING) return fail(MOE_ERR_SLOT_STATE, "slot %d is Filling", slot);
+    if (a->owner[slot] >= 0) a->slot_of[a->owner[slot]] = -1;
+    a->owner[slot] = -1;
+    a->state[slot] = MOE_SLOT_AVAILABLE;
+    return MOE_OK;
+}
+
+moe_status arena_phi(const moe_arena *a, int32_t *phi, int32_t n)
+{
+    if (!a || !phi) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+    const int ne = a->shape.E + a->shape.n_shared;
+    if (n < ne) return fail(MOE_ERR_INVALID_ARG, "phi needs %d entries", ne);
+    for (int e = 0; e < n; ++e) phi[e] = -1;
+    for (int s = 0; s < a->shape.P; ++s)
+        if (a->state[s] == MOE_SLOT_READY || a->state[s] == MOE_SLOT_IN_USE) phi[a->owner[s]] = s;
+    return MOE_OK;
+}
+
+moe_status arena_slot_info(const moe_arena *a, int32_t slot, int32_t *state, int32_t *expert)
+{
+    if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
+    if (slot < 0 || slot >= a->shape.P) return fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, P)", slot);
+    if (state) *state = a->state[slot];
+    if (expert) *expert = a->owner[slot];
+    return MOE_OK;
+}
+
+moe_status moe_selftest_mfma_layout(float *out, moe_stream stream)
+{
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    HIP_TRY(launch_selftest_mfma(out, S(stream)), "self-test launch");
+    return MOE_OK;
+}
+
+moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float *W_r, const float *bias,
+                             const float *logits, float *Y, moe_arena *arena, const void *const *host_gu,
+                             const void *const *host_d, const moe_routes *routes, void *ws, size_t ws_bytes,
+                             moe_stream compute, moe_stream copy)
+{
+    MOE_TRY(check_shape(shape));
+    if (shape->T == 0) return MOE_OK;  // an empty prompt: nothing to do
+    MOE_TRY(check_routes(routes));
+    WsLayout w;
+    MOE_TRY(check_ws(shape, ws, ws_bytes, &w));
+    if (!X || !Y || !arena) return fail(MOE_ERR_INVALID_ARG, "layer: X, Y and arena are required");
+    if (!W_r && !logits) return fail(MOE_ERR_INVALID_ARG, "layer: give W_r or logits");
+    if (!aligned(Y, 16) || (shape->dtype == MOE_DT_BF16 && !aligned(X, 16)))
+        return fail(MOE_ERR_INVALID_ARG, "layer: X and Y must be 16-byte aligned");
+    if ((host_gu == nullptr) != (host_d == nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "layer: give both host_gu and host_d, or neither");
+    if (arena->shape.d != shape->d || arena->shape.f != shape->f || arena->shape.P != shape->P ||
+        arena->shape.dtype != shape->dtype || arena->shape.E != shape->E || arena->shape.n_shared != shape->n_shared)
+        return fail(MOE_ERR_INVALID_ARG, "arena was made for another shape");
+    const moe_shape &s = *shape;
+    const int kp = s.k + s.n_shared, ne = s.E + s.n_shared;
+    hipStream_t cs = S(compute), ps = copy ? S(copy) : cs;
+    const float *L = logits;
+    if (W_r) {
+        L = ws_at<float>(ws, w.logits);
+        HIP_TRY(launch_router_logits(s, X, W_r, bias, ws_at<float>(ws, w.logits), cs), "router launch");
+    }
+    std::vector<int32_t> phi(kMaxExp, -1);
+    PhiArg pa;
+
+    if (!host_gu) {
+        // Resident layer: every expert must be Ready in the arena.
+        MOE_TRY(arena_phi(arena, phi.data(), ne));
+        for (int e = 0; e < ne; ++e)
+            if (phi[e] < 0) return fail(MOE_ERR_SLOT_STATE, "expert %d is not resident", e);
+        MOE_TRY(check_phi(shape, phi.data(), &pa));
+        const int tc = (int)std::min<int64_t>(s.T, s.capacity / kp);
+        if (s.T > 0 && tc < 1) return fail(MOE_ERR_CAPACITY, "capacity %d below one token's %d routes", s.capacity, kp);
+        std::lock_guard<std::mutex> lk(arena->mu);
+        MOE_TRY(arena_acquire(arena, phi.data(), cs));
+        for (int t0 = 0; t0 < s.T; t0 += tc) {
+            const int nt = std::min(tc, s.T - t0);
+            MOE_TRY(route_build_impl(s, w, t0, nt, L, pa, MOE_ROUTE_RESET, *routes, ws, cs));
+            MOE_TRY(experts_impl(s, w, X, *routes, arena, nt * kp, false, ws, cs));
+        }
+        MOE_TRY(arena_release_after(arena, phi.data(), cs));
+        HIP_TRY(launch_combine(s, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), cs), "combine launch");
+        return MOE_OK;
+    }
+
+    // Paged layer (sections 3.3-3.4): route once, read the per-expert route
+    // counts (the one host synchronization), then stream the groups that have
+    // routes through the banks: group g of G experts (expert e is member
+    // r(e) = e mod G of group e / G; the permutation pi is the identity) goes
+    // to bank b = (sequence number mod B), slots b*G + r(e) (Eq. 4). Loads run
+    // on the copy stream, each after the bank's previous release; each group's
+    // route build and expert FFN run on the compute stream after the load.
+    if ((int64_t)s.T * kp > s.capacity)
+        return fail(MOE_ERR_CAPACITY, "paging needs capacity >= T*K' (%lld)", (long long)s.T * kp);
+    const int G = arena->G, B = s.P / G;
+    HIP_TRY(launch_topk(s, 0, s.T, L, routes->topk_idx, routes->topk_w, ws_at<int32_t>(ws, w.done), cs), "top-k launch");
+    HIP_TRY(launch_expert_hist(s, routes->topk_idx, (int64_t)s.T * kp, ws_at<int32_t>(ws, w.ecount), cs),
+            "histogram launch");
+    std::vector<int32_t> ecount(ne, 0);
+    HIP_TRY(hipMemcpyAsync(ecount.data(), ws_at<int32_t>(ws, w.ecount), ne * 4, hipMemcpyDeviceToHost, cs),
+            "hipMemcpyAsync");
+    HIP_TRY(hipStreamSynchronize(cs), "hipStreamSynchronize");
+    for (int e = 0; e < ne; ++e)
+        if (!host_gu[e] || !host_d[e]) return fail(MOE_ERR_INVALID_ARG, "host expert %d pointer is NULL", e);
+    std::lock_guard<std::mutex> lk(arena->mu);
+    for (int sl = 0; sl < s.P; ++sl) {  // forget the previous layer's mapping
+        if (arena->owner[sl] >= 0) arena->slot_of[arena->owner[sl]] = -1;
+        arena->owner[sl] = -1;
+        arena->state[sl] = MOE_SLOT_AVAILABLE;
+    }
+    const int ngroups = (ne + G - 1) / G;
+    int seq = 0;
+    for (int g = 0; g < ngroups; ++g) {
+        int routed = 0;
+        for (int e = g * G; e < std::min(ne, (g + 1) * G); ++e) routed += ecount[e];
+        if (routed == 0) continue;  // a group with no routes is never loaded
+        const int b = seq++ % B;
+        std::fill(phi.begin(), phi.end(), -1);
+        for (int e = g * G; e < std::min(ne, (g + 1) * G); ++e) {
+            if (ecount[e] == 0) continue;
+            const int slot = b * G + (e % G);
+            MOE_TRY(arena_bind_locked(arena, slot, e, host_gu[e], host_d[e], ps));
+            phi[e] = slot;
+        }
+        MOE_TRY(check_phi(shape, phi.data(), &pa));
+        MOE_TRY(arena_acquire(arena, phi.data(), cs));
+        MOE_TRY(route_build_impl(s, w, 0, s.T, nullptr, pa, 0, *routes, ws, cs));
+        MOE_TRY(experts_impl(s, w, X, *routes, arena, s.T * kp, false, ws, cs));
+        MOE_TRY(arena_release_after(arena, phi.data(), cs));
+    }
+    HIP_TRY(launch_combine(s, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), cs), "combine launch");
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Weighted combine into the token accumulator (EStream Eq. 2:
+// Y_t = A_t + sum over the token's routes of alpha F_e(X_t)), gate/up
+// packing (section 3.3, offline layout for the consuming kernel), and an
+// MFMA lane-layout self-test.
+//
+// Combine: Y holds A_t on entry. Each thread owns 4 consecutive columns of
+// one token row and adds the token's computed route rows Yr[t*K' + j] in
+// ascending j, so the fp32 sum order is fixed: no atomics, bitwise
+// reproducible, and independent of how routes were spread over slots,
+// workgroups or invocations.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void k_combine(float *__restrict__ Y, int64_t ldy,
+                                                 const float *__restrict__ Yr,
+                                                 const int32_t *__restrict__ done, int d, int kp)
+{
+    const int t = blockIdx.y;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c >= d) return;
+    float4 y = *(const float4 *)(Y + (int64_t)t * ldy + c);
+    for (int j = 0; j < kp; ++j) {
+        const int64_t i = (int64_t)t * kp + j;
+        if (done[i]) {
+            const float4 v = *(const float4 *)(Yr + i * d + c);
+            y.x += v.x;
+            y.y += v.y;
+            y.z += v.z;
+            y.w += v.w;
+        }
+    }
+    *(float4 *)(Y + (int64_t)t * ldy + c) = y;
+}
+
+// dst row r of expert e: q = r / 64, w = r % 64; gate row 32q + w for w < 32,
+// up row 32q + w - 32 otherwise. One workgroup copies one row as 32-bit words.
+__global__ __launch_bounds__(256) void k_pack_gate_up(const uint32_t *__restrict__ Wg,
+                                                      const uint32_t *__restrict__ Wu,
+                                                      uint32_t *__restrict__ dst, int64_t row_words,
+                                                      int64_t src_stride_w, int64_t dst_stride_w)
+{
+    const int r = blockIdx.x;
+    const int e = blockIdx.y;
+    const int q = r >> 6, w = r & 63;
+    const uint32_t *src = (w < 32 ? Wg + (int64_t)(32 * q + w) * row_words
+                                  : Wu + (int64_t)(32 * q + w - 32) * row_words) +
+                          (int64_t)e * src_stride_w;
+    uint32_t *out = dst + (int64_t)e * dst_stride_w + (int64_t)r * row_words;
+    for (int64_t c = threadIdx.x; c < row_words; c += 256) out[c] = src[c];
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// One wave. A[i][k] and B[k][j] (32x16 and 16x32) with small integer values
+// are placed in the operand registers under the assumed layout (lane l: row
+// or column l % 32, k = 8*(l/32) .. +7); the result registers are written to
+// out[32][32] under the assumed output layout (register r of lane l -> row
+// 8*(r/4) + 4*(l/32) + r%4, column l % 32). The host checks out == A*B, which
+// holds only if the assumed layouts are the hardware's.
+__global__ void k_selftest_mfma(float *out)
+{
+    const int l = threadIdx.x;
+    bf16x8_t av, bv;
+    for (int q = 0; q < 8; ++q) {
+        const int k = 8 * (l >> 5) + q;
+        const int i = l & 31;
+        const float aval = (float)((i * 3 + k * 5) % 7 - 3);        // A[i][k]
+        const float bval = (float)((k * 2 + (l & 31) * 7) % 5 - 2);  // B[k][j], j = l % 32
+        av[q] = (__bf16)aval;
+        bv[q] = (__bf16)bval;
+    }
+    f32x16_t acc;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        out[row * 32 + (l & 31)] = acc[r];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_shape &s, float *Y, const float *Yr, const int32_t *done,
+                          hipStream_t st)
+{
+    if (s.T == 0) return hipSuccess;
+    const dim3 grid((unsigned)((s.d / 4 + 255) / 256), (unsigned)s.T);
+    hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, Y, s.ldy, Yr, done, s.d,
+                       s.k + s.n_shared);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_gate_up(const moe_shape &s, const void *Wg, const void *Wu, void *dst,
+                               int n, int64_t src_stride, int64_t dst_stride, hipStream_t st)
+{
+    if (n == 0) return hipSuccess;
+    const int esz = s.dtype == MOE_DT_BF16 ? 2 : 4;
+    const int64_t row_words = (int64_t)s.d * esz / 4;
+    const int64_t ssw = src_stride * esz / 4, dsw = dst_stride * esz / 4;
+    hipLaunchKernelGGL(k_pack_gate_up, dim3((unsigned)(2 * s.f), (unsigned)n), dim3(256), 0, st,
+                       (const uint32_t *)Wg, (const uint32_t *)Wu, (uint32_t *)dst, row_words, ssw,
+                       dsw);
+    return hipGetLastError();
+}
+
+hipError_t launch_selftest_mfma(float *out, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_selftest_mfma, dim3(1), dim3(64), 0, st, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,102 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kRouteBlock = 256;      // routes per counting block
+constexpr int kMaxExp = MOE_MAX_EXPERTS;
+
+// Placement map passed by value in the kernel arguments (2 KB).
+struct PhiArg {
+    int32_t v[kMaxExp];
+};
+
+// Byte offsets of the workspace regions for one shape.
+struct WsLayout {
+    size_t err;      // int32[64]: [0] device error word
+    size_t ecount;   // int32[kMaxExp]: routes per logical expert (paging)
+    size_t blk;      // int32[nblk][P]: per-block slot counts, then bases
+    size_t rank;     // int32[C]: in-block stable rank of each route of a build
+    size_t done;     // int32[T*K']: 1 once route i's Yr row is computed
+    size_t logits;   // float[T][E]
+    size_t H;        // dtype[C][f]
+    size_t Yr;       // float[T*K'][d]
+    size_t total;
+    int nblk;        // ceil(C / kRouteBlock)
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline WsLayout ws_layout(const moe_shape &s)
+{
+    WsLayout w{};
+    const size_t kp = (size_t)(s.k + s.n_shared);
+    const size_t esz = s.dtype == MOE_DT_BF16 ? 2 : 4;
+    w.nblk = (s.capacity + kRouteBlock - 1) / kRouteBlock;
+    size_t o = 0;
+    w.err = o;    o = align_up(o + 64 * 4, 256);
+    w.ecount = o; o = align_up(o + kMaxExp * 4, 256);
+    w.blk = o;    o = align_up(o + (size_t)w.nblk * s.P * 4, 256);
+    w.rank = o;   o = align_up(o + (size_t)s.capacity * 4, 256);
+    w.done = o;   o = align_up(o + (size_t)s.T * kp * 4, 256);
+    w.logits = o; o = align_up(o + (size_t)s.T * s.E * 4, 256);
+    w.H = o;      o = align_up(o + (size_t)s.capacity * s.f * esz, 256);
+    w.Yr = o;     o = align_up(o + (size_t)s.T * kp * s.d * 4, 256);
+    w.total = o;
+    return w;
+}
+
+// Arguments of the grouped expert GEMMs (gate/up + SwiGLU, and down).
+// Per slot s the weight slice is B + s * slot_stride, an [N][K] row-major
+// matrix; rows of A are gathered X rows (gate/up) or consecutive H rows
+// (down) in record order.
+struct GemmArgs {
+    const int32_t *slot_offset;  // [P+1]
+    int P;
+    const int32_t *rec_token;    // [C]
+    const int32_t *rec_route;    // [C]
+    const void *A;               // X (gate/up) or H (down)
+    int64_t lda;                 // ldx or f
+    const void *B;               // plane base
+    int64_t slot_stride;         // elements
+    int N, K;
+    void *C;                     // H (gate/up) or Yr (down)
+    int64_t ldc;                 // f or d
+    const float *topk_w;         // down: weight of route i
+    int32_t *done;               // down: computed marks
+};
+
+// ---- launchers (return hipError_t of the launch) ----
+hipError_t launch_router_logits(const moe_shape &s, const void *X, const float *Wr,
+                                const float *bias, float *L, hipStream_t st);
+hipError_t launch_topk(const moe_shape &s, int t0, int nt, const float *L, int32_t *idx,
+                       float *w, int32_t *done, hipStream_t st);
+hipError_t launch_route_count(const moe_shape &s, int64_t i0, int64_t n, const int32_t *idx,
+                              const PhiArg &phi, int32_t *blk, int32_t *rank, int32_t *err,
+                              int32_t *done, int reset, hipStream_t st);
+hipError_t launch_route_scan(const moe_shape &s, int nblk, int32_t *blk, int32_t *count,
+                             int32_t *offset, hipStream_t st);
+hipError_t launch_route_place(const moe_shape &s, int64_t i0, int64_t n, const int32_t *idx,
+                              const PhiArg &phi, const int32_t *blk, const int32_t *rank,
+                              int32_t *rec_token, int32_t *rec_route, int32_t *route_pos,
+                              hipStream_t st);
+hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
+                          hipStream_t st);
+hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
+                       hipStream_t st);
+hipError_t launch_combine(const moe_shape &s, float *Y, const float *Yr, const int32_t *done,
+                          hipStream_t st);
+hipError_t launch_pack_gate_up(const moe_shape &s, const void *Wg, const void *Wu, void *dst,
+                               int n, int64_t src_stride, int64_t dst_stride, hipStream_t st);
+hipError_t launch_selftest_mfma(float *out, hipStream_t st);
+hipError_t launch_fill_i32(int32_t *p, int32_t v, int64_t n, hipStream_t st);
+hipError_t launch_expert_hist(const moe_shape &s, const int32_t *idx, int64_t n, int32_t *count,
+                              hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,91 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+the CPU oracle on the same seeded inputs, and compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import oracle as oracle_mod
+from routed_expert_ffn_top_amd import binding as B
+from routed_expert_ffn_top_amd.inputs import LayerInputs, MoEConfig, make_inputs
+
+TOL = {"bf16": 1e-2, "f32": 1e-5}
+ALPHA_TOL = 1e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def np32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def rel_err(y: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.max(np.abs(y.astype(np.float64) - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def gpu_inputs(cfg: MoEConfig, layer=0) -> LayerInputs:
+    return make_inputs(cfg, layer=layer, device="cuda")
+
+
+class OracleRun:
+    """Oracle results for one layer's inputs (weights widened to fp32)."""
+
+    def __init__(self, inp: LayerInputs, logits=None):
+        self.cfg = cfg = inp.cfg
+        self.orc = oracle_mod.get()
+        self.X = np32(inp.X)
+        self.Wr = np32(inp.Wr)
+        self.bias = None if inp.bias is None else np32(inp.bias)
+        self.A = np32(inp.A)
+        self.L = self.orc.router_logits(self.X, self.Wr, self.bias) if logits is None else logits
+        self.idx, self.alpha = self.orc.topk(self.L, cfg.k, cfg.n_shared, cfg.renorm)
+        self._w = None
+        self._inp = inp
+
+    def weights(self):
+        if self._w is None:
+            self._w = (np32(self._inp.Wg), np32(self._inp.Wu), np32(self._inp.Wd))
+        return self._w
+
+    def route_map(self, phi, P, t0=0, nt=None):
+        return self.orc.route_map(self.idx, np.asarray(phi, dtype=np.int32), P, t0, nt)
+
+    def Y(self, tokens=None, route_mask=None):
+        Wg, Wu, Wd = self.weights()
+        return self.orc.expert_ffn(self.X, self.idx, self.alpha, Wg, Wu, Wd, self.A,
+                                   tokens=tokens, route_mask=route_mask)
+
+
+def check_descriptors(routes: dict, ref: dict, n_valid_expected=None):
+    cnt = routes["slot_count"].cpu().numpy()
+    off = routes["slot_offset"].cpu().numpy()
+    assert np.array_equal(cnt, ref["count"]), "slot_count differs"
+    assert np.array_equal(off, ref["offset"]), "slot_offset differs"
+    n = int(off[-1])
+    assert n == ref["n_valid"]
+    if n_valid_expected is not None:
+        assert n == n_valid_expected
+    assert np.array_equal(routes["rec_token"][:n].cpu().numpy(), ref["rec_token"]), "rec_token differs"
+    assert np.array_equal(routes["rec_route"][:n].cpu().numpy(), ref["rec_route"]), "rec_route differs"
+    assert np.array_equal(routes["route_pos"].cpu().numpy(), ref["route_pos"]), "route_pos differs"
+
+
+def check_topk(routes: dict, orun: OracleRun):
+    idx = routes["topk_idx"].cpu().numpy()
+    assert np.array_equal(idx, orun.idx), "top-k ids differ"
+    w = routes["topk_w"].cpu().numpy().astype(np.float64)
+    rel = np.max(np.abs(w - orun.alpha) / np.maximum(np.abs(orun.alpha), 1e-30))
+    assert rel <= ALPHA_TOL, f"alpha rel err {rel}"
+
+
+def sample_tokens(T: int, n: int, seed: int = 7) -> np.ndarray:
+    if n >= T:
+        return np.arange(T, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=n - 2, replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(pick), dtype=np.int64)

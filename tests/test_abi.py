@@ -1,0 +1,186 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/moe.h declares, and its host-side checks and host-only helpers
+behave as documented. No GPU work is launched here: every call below fails
+its argument check before any HIP call, or is host-only."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from routed_expert_ffn_top_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s*\b([a-z_][a-z0-9_]*)\s*\(", text, re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "for", "sizeof")))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("moe_route_build", "moe_expert_ffn", "moe_layer_prefill", "arena_bind_slot"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.load()._name)
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(_declared_functions()) <= set(B._SIGS), "binding lacks a declared function"
+
+
+def test_version_and_error_channel():
+    assert "gfx950" in B.moe_version()
+    bad = B.make_shape(T=8, d=100, f=256, E=8, k=2, dtype="bf16")
+    assert B.moe_workspace_bytes(bad) == 0
+    st, msg = B.moe_last_error()
+    assert st == B.MOE_ERR_UNSUPPORTED and "d % 64" in msg
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(k=9), B.MOE_ERR_INVALID_ARG),
+    (dict(P=0), B.MOE_ERR_INVALID_ARG),
+    (dict(P=513), B.MOE_ERR_INVALID_ARG),
+    (dict(n_shared=600), B.MOE_ERR_INVALID_ARG),
+    (dict(capacity=0), B.MOE_ERR_INVALID_ARG),
+    (dict(ldx=64), B.MOE_ERR_INVALID_ARG),
+    (dict(ldy=130), B.MOE_ERR_INVALID_ARG),
+    (dict(f=96), B.MOE_ERR_UNSUPPORTED),
+    (dict(ldx=132), B.MOE_ERR_UNSUPPORTED),
+])
+def test_shape_checks(kw, status):
+    base = dict(T=16, d=128, f=256, E=8, k=2, dtype="bf16")
+    base.update(kw)
+    s = B.make_shape(**base)
+    assert B.moe_workspace_bytes(s) == 0
+    assert B.moe_last_error()[0] == status
+
+
+def test_workspace_holds_the_big_buffers():
+    for (T, d, f, E, k, S, dt) in [(4096, 2048, 1024, 64, 8, 0, "bf16"), (64, 128, 256, 8, 2, 0, "f32"),
+                                   (4096, 2048, 1408, 64, 6, 2, "bf16")]:
+        s = B.make_shape(T=T, d=d, f=f, E=E, k=k, n_shared=S, dtype=dt)
+        n = B.moe_workspace_bytes(s)
+        esz = 2 if dt == "bf16" else 4
+        kp = k + S
+        assert n >= T * kp * d * 4 + T * kp * f * esz + T * E * 4
+        assert n % 256 == 0
+
+
+def _fake_routes(shape):
+    # distinct fake device addresses: never dereferenced, the calls fail first
+    return {k: 0x10000 * (i + 1) for i, k in enumerate(
+        ("topk_idx", "topk_w", "slot_count", "slot_offset", "rec_token", "rec_route", "route_pos"))}
+
+
+class _FakeWs:
+    def __init__(self, n, addr=0x7f0000000000):
+        self.n, self.addr = n, addr
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+    def data_ptr(self):
+        return self.addr
+
+
+def test_route_build_argument_checks():
+    s = B.make_shape(T=16, d=128, f=256, E=8, k=2, dtype="bf16", capacity=32)
+    ws = _FakeWs(B.moe_workspace_bytes(s))
+    r = _fake_routes(s)
+    phi = list(range(8))
+    with pytest.raises(B.MoEError) as ei:       # duplicate slot in phi
+        B.moe_route_build(s, 0, 16, None, [0, 0, 1, 2, 3, 4, 5, 6], 0, r, ws, 0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoEError) as ei:       # slot outside [-1, P)
+        B.moe_route_build(s, 0, 16, None, [0, 1, 2, 3, 4, 5, 6, 8], 0, r, ws, 0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    s2 = B.make_shape(T=16, d=128, f=256, E=8, k=2, dtype="bf16", capacity=31)
+    ws2 = _FakeWs(B.moe_workspace_bytes(s2))
+    with pytest.raises(B.MoEError) as ei:       # 16 tokens x 2 routes > 31
+        B.moe_route_build(s2, 0, 16, None, phi, 0, r, ws2, 0)
+    assert ei.value.status == B.MOE_ERR_CAPACITY
+    with pytest.raises(B.MoEError) as ei:       # token range outside [0, T)
+        B.moe_route_build(s, 10, 7, None, phi, 0, r, ws, 0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoEError) as ei:       # workspace too small
+        B.moe_route_build(s, 0, 16, None, phi, 0, r, _FakeWs(ws.n - 256), 0)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE
+    with pytest.raises(B.MoEError) as ei:       # misaligned workspace
+        B.moe_route_build(s, 0, 16, None, phi, 0, r, _FakeWs(ws.n, 0x7f0000000010), 0)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE
+    r0 = dict(r, rec_route=0)
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_route_build(s, 0, 16, None, phi, 0, r0, ws, 0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+
+
+def test_pack_gate_up_host_layout():
+    """Rows 64q..64q+31 of the packed slice are gate rows 32q..32q+31, rows
+    64q+32..64q+63 are up rows 32q..32q+31 (the layout include/moe.h states)."""
+    f, d = 96 * 2, 64
+    s = B.make_shape(T=4, d=d, f=f, E=4, k=1, dtype="f32")
+    rng = np.random.default_rng(0)
+    Wg = torch.from_numpy(rng.standard_normal((f, d), dtype=np.float32))
+    Wu = torch.from_numpy(rng.standard_normal((f, d), dtype=np.float32))
+    out = torch.empty((2 * f, d), dtype=torch.float32)
+    B.moe_pack_gate_up_host(s, Wg, Wu, out)
+    for q in range(f // 32):
+        assert torch.equal(out[64 * q:64 * q + 32], Wg[32 * q:32 * q + 32])
+        assert torch.equal(out[64 * q + 32:64 * q + 64], Wu[32 * q:32 * q + 32])
+    sb = B.make_shape(T=4, d=d, f=f, E=4, k=1, dtype="bf16")
+    outb = torch.empty((2 * f, d), dtype=torch.bfloat16)
+    B.moe_pack_gate_up_host(sb, Wg.bfloat16(), Wu.bfloat16(), outb)
+    assert torch.equal(outb[32:64], Wu[:32].bfloat16())
+
+
+class _FakeArena:
+    def __init__(self, handle):
+        self.handle = handle
+
+
+def test_arena_table_on_host():
+    s = B.make_shape(T=16, d=128, f=256, E=8, k=2, P=4, dtype="bf16")
+    with pytest.raises(B.MoEError):
+        B.moe_arena_create(s, 0x100000, 0x200000, 2 * 256 * 128, 256 * 128, 3)  # P % G != 0
+    with pytest.raises(B.MoEError):
+        B.moe_arena_create(s, 0x100000, 0x200000, 10, 256 * 128, 2)             # stride too small
+    h = B.moe_arena_create(s, 0x100000, 0x40000000, 2 * 256 * 128, 256 * 128, 2)
+    a = _FakeArena(h)
+    try:
+        for slot in range(4):
+            assert B.arena_slot_info(a, slot) == (B.MOE_SLOT_AVAILABLE, -1)
+        assert B.arena_phi(a, 8) == [-1] * 8
+        B.arena_release_slot(a, 1)   # releasing an Available slot is harmless
+        with pytest.raises(B.MoEError) as ei:
+            B.arena_slot_info(a, 4)
+        assert ei.value.status == B.MOE_ERR_INVALID_ARG
+        with pytest.raises(B.MoEError) as ei:
+            B.arena_bind_slot(a, 5, 0, 0x1000, 0x2000, 0)
+        assert ei.value.status == B.MOE_ERR_INVALID_ARG
+        with pytest.raises(B.MoEError) as ei:
+            B.arena_bind_slot(a, 0, 8, 0x1000, 0x2000, 0)   # expert id outside [0, E)
+        assert ei.value.status == B.MOE_ERR_INVALID_ARG
+        # an invocation naming a slot that is not Ready is refused before any work
+        ws = _FakeWs(B.moe_workspace_bytes(s))
+        with pytest.raises(B.MoEError) as ei:
+            B.moe_expert_ffn(s, 0x1000, 0x2000, _fake_routes(s), a, [0, 1, 2, 3, -1, -1, -1, -1],
+                             B.MOE_FFN_EXPERTS, ws, 0)
+        assert ei.value.status == B.MOE_ERR_SLOT_STATE
+        # a map with a slot shared by two experts is refused too
+        with pytest.raises(B.MoEError) as ei:
+            B.moe_expert_ffn(s, 0x1000, 0x2000, _fake_routes(s), a, [0, 0, -1, -1, -1, -1, -1, -1],
+                             B.MOE_FFN_EXPERTS, ws, 0)
+        assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    finally:
+        B.moe_arena_destroy(h)

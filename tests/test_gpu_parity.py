@@ -1,0 +1,280 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: router logits, top-k ids, slot counts and offsets, records
+(rec_token, rec_route), route_pos, n_valid. Tolerance: route weights alpha
+(relative 1e-6: expf and the softmax sum order differ), layer output
+max|y - y_ref| / max|y_ref| <= 1e-2 for bf16 layers and 1e-5 for the fp32
+layer. Inputs are the seeded synthetic workloads of inputs.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (OracleRun, TOL, check_descriptors, check_topk, gpu_inputs, np32, rel_err,
+                      sample_tokens, say)
+from routed_expert_ffn_top_amd import binding as B
+from routed_expert_ffn_top_amd.inputs import CONFIGS, MoEConfig, make_inputs, make_logits, random_phi
+from routed_expert_ffn_top_amd.layer import MoELayer
+
+pytestmark = pytest.mark.gpu
+
+# a mid-size bf16 layer the oracle finishes in about a second: several tiles
+# per slot and ragged tails (T*k = 2400 routes over 16 experts)
+MID = MoEConfig(name="mid_bf16", index=9, T=300, d=512, f=384, E=16, k=8)
+MID_SHARED = MoEConfig(name="mid_shared", index=10, T=200, d=256, f=192, E=12, k=3, n_shared=2,
+                       renorm=False)
+
+
+def _layer_out(layer: MoELayer, inp, logits=None):
+    Y = inp.A.clone()
+    layer.forward(Y, logits=logits)
+    torch.cuda.synchronize()
+    return Y
+
+
+def test_mfma_lane_layout():
+    say("mfma layout self-test")
+    out = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    B.moe_selftest_mfma_layout(out)
+    torch.cuda.synchronize()
+    i = np.arange(32)[:, None]
+    k = np.arange(16)[None, :]
+    A = ((3 * i + 5 * k) % 7 - 3).astype(np.float64)
+    kk = np.arange(16)[:, None]
+    j = np.arange(32)[None, :]
+    Bm = ((2 * kk + 7 * j) % 5 - 2).astype(np.float64)
+    assert np.array_equal(out.cpu().numpy().reshape(32, 32), A @ Bm)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "olmoe_t1024", "virt_olmoe_t256", "mixtral_t256"])
+def test_router_logits_bitexact(name):
+    cfg = CONFIGS[name]
+    if name == "mixtral_t256":
+        cfg = cfg.with_(T=96, f=64)  # router only: keep the expert weights small
+    say("router", name)
+    inp = gpu_inputs(cfg)
+    s = B.make_shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.n_shared, dtype=cfg.dtype)
+    L = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
+    B.moe_router_logits(s, inp.X, inp.Wr, inp.bias, L)
+    torch.cuda.synchronize()
+    orc = OracleRun(inp)
+    assert np.array_equal(L.cpu().numpy().view(np.int32), orc.L.view(np.int32))
+
+
+ROUTE_CASES = {
+    # (T, E, k, n_shared, renorm, P, absent, t0, nt, logit kind)
+    "olmoe": (1024, 64, 8, 0, True, 64, 0, 0, 1024, "normal"),
+    "dsv2": (4096, 64, 6, 2, False, 66, 0, 0, 4096, "normal"),
+    "mixtral": (4096, 8, 2, 0, True, 8, 0, 0, 4096, "normal"),
+    "ties": (777, 16, 4, 0, True, 16, 0, 0, 777, "ties"),
+    "k_eq_E": (130, 8, 8, 0, True, 8, 0, 0, 130, "normal"),
+    "k1": (257, 32, 1, 0, True, 32, 0, 0, 257, "normal"),
+    "partial_phi": (1000, 64, 8, 0, True, 16, 48, 0, 1000, "normal"),
+    "wide_P": (513, 20, 3, 1, True, 100, 0, 0, 513, "normal"),
+    "range": (600, 64, 8, 0, True, 64, 0, 123, 200, "normal"),
+    "one_token": (1, 64, 8, 0, True, 64, 0, 0, 1, "normal"),
+    "skewed": (2048, 64, 8, 0, True, 64, 0, 0, 2048, "skewed"),
+}
+
+
+@pytest.mark.parametrize("case", list(ROUTE_CASES))
+def test_route_build_bitexact(case):
+    T, E, k, S, renorm, P, absent, t0, nt, kind = ROUTE_CASES[case]
+    say("route build", case)
+    L = make_logits(T, E, seed=100 + len(case))
+    if kind == "ties":
+        L = torch.round(L * 2) / 2      # many exactly equal logits
+    if kind == "skewed":
+        L[:, 5] += 6.0                  # nearly every token picks expert 5
+        L[:, 9] -= 30.0                 # expert 9 is never picked
+    ne = E + S
+    phi = list(range(ne)) if (P == ne and absent == 0) else random_phi(ne, P, seed=3, n_absent=absent).tolist()
+    cap = max(1, nt * (k + S))
+    s = B.make_shape(T, 64, 64, E, k, S, P=P, capacity=cap, dtype="bf16", renorm=renorm)
+    routes = B.alloc_routes(s)
+    ws = B.alloc_workspace(s)
+    Ld = L.cuda()
+    B.moe_route_build(s, t0, nt, Ld, phi, 0, routes, ws)
+    torch.cuda.synchronize()
+    from oracle import oracle as oracle_mod
+    orc = oracle_mod.get()
+    idx, alpha = orc.topk(L.numpy(), k, S, renorm)
+    kp = k + S
+    gi = routes["topk_idx"].cpu().numpy()[t0:t0 + nt]
+    assert np.array_equal(gi, idx[t0:t0 + nt])
+    gw = routes["topk_w"].cpu().numpy()[t0:t0 + nt].astype(np.float64)
+    aref = alpha[t0:t0 + nt]
+    assert np.max(np.abs(gw - aref) / np.maximum(aref, 1e-30)) <= 1e-6
+    full_idx = routes["topk_idx"].cpu().numpy()
+    ref = orc.route_map(full_idx, np.array(phi, dtype=np.int32), P, t0, nt,
+                        route_pos=np.full(T * kp, -1, dtype=np.int32))
+    check_descriptors(routes, ref)
+    assert B.moe_device_errors(s, ws) == 0
+
+
+def test_route_build_flags_bad_expert_ids():
+    say("route build with an out-of-range supplied id")
+    T, E, k = 64, 8, 2
+    s = B.make_shape(T, 64, 64, E, k, dtype="bf16")
+    routes = B.alloc_routes(s)
+    ws = B.alloc_workspace(s)
+    idx = torch.stack([torch.arange(T) % E, (torch.arange(T) + 1) % E], 1).to(torch.int32)
+    idx[5, 1] = 99
+    routes["topk_idx"].copy_(idx)
+    B.moe_route_build(s, 0, T, None, list(range(E)), B.MOE_ROUTE_RESET, routes, ws)
+    torch.cuda.synchronize()
+    assert B.moe_device_errors(s, ws) == B.MOE_DEVERR_EXPERT_ID
+    assert int(routes["slot_offset"][-1]) == T * k - 1
+    assert int(routes["route_pos"][5 * k + 1]) == -1
+    assert B.moe_device_errors(s, ws) == 0  # cleared
+
+
+def _check_layer(cfg, tokens=None, simple=False, **layer_kw):
+    inp = gpu_inputs(cfg)
+    layer = MoELayer(inp, **layer_kw)
+    Y = inp.A.clone()
+    if simple:
+        _run_steps(layer, Y, simple=True)
+    else:
+        layer.forward(Y)
+    torch.cuda.synchronize()
+    orun = OracleRun(inp)
+    check_topk(layer.routes, orun)
+    if layer.shape.capacity >= cfg.T * cfg.kp and not layer.paged:
+        ref = orun.route_map(layer.phi, layer.shape.P)
+        check_descriptors(layer.routes, ref, n_valid_expected=cfg.T * cfg.kp)
+    toks = np.arange(cfg.T) if tokens is None else tokens
+    yref = orun.Y(tokens=toks)
+    err = rel_err(np32(Y)[toks], yref)
+    say(f"  {cfg.name}: rel err {err:.3e}")
+    assert err <= TOL[cfg.dtype], err
+    return Y, layer, inp
+
+
+def _run_steps(layer: MoELayer, Y, simple=False):
+    """The layer as separate calls: router, route build, expert FFN, combine."""
+    s = layer.shape
+    L = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    B.moe_router_logits(s, layer.X, layer.Wr, layer.bias, L)
+    B.moe_route_build(s, 0, s.T, L, layer.phi, 0, layer.routes, layer.ws)
+    flags = B.MOE_FFN_EXPERTS | B.MOE_FFN_FINALIZE | (B.MOE_FFN_SIMPLE_KERNEL if simple else 0)
+    B.moe_expert_ffn(s, layer.X, Y, layer.routes, layer.arena, layer.phi, flags, layer.ws)
+
+
+def test_layer_tiny_fp32():
+    say("layer tiny fp32")
+    _check_layer(CONFIGS["tiny_fp32"])
+
+
+def test_layer_mid_bf16():
+    say("layer mid bf16")
+    _check_layer(MID)
+
+
+def test_layer_mid_bf16_simple_kernel():
+    say("layer mid bf16, plain kernel")
+    _check_layer(MID, simple=True)
+
+
+def test_layer_shared_experts():
+    say("layer with shared experts")
+    _check_layer(MID_SHARED)
+
+
+def test_layer_olmoe_t1024():
+    say("layer OLMoE T=1024")
+    _check_layer(CONFIGS["olmoe_t1024"])
+
+
+def test_layer_dsv2lite_t4096_sampled():
+    say("layer DSV2-Lite T=4096 (sampled rows)")
+    cfg = CONFIGS["dsv2lite_t4096"]
+    _check_layer(cfg, tokens=sample_tokens(cfg.T, 96))
+
+
+def test_layer_olmoe_t4096_sampled():
+    say("layer OLMoE T=4096 (sampled rows)")
+    cfg = CONFIGS["olmoe_t4096"]
+    _check_layer(cfg, tokens=sample_tokens(cfg.T, 96))
+
+
+def test_layer_mixtral_t256_sampled():
+    say("layer Mixtral T=256 (sampled rows)")
+    cfg = CONFIGS["mixtral_t256"]
+    _check_layer(cfg, tokens=sample_tokens(cfg.T, 24))
+
+
+def test_deterministic_and_phi_independent():
+    say("determinism, capacity split, phi permutation")
+    inp = gpu_inputs(MID)
+    base = MoELayer(inp)
+    y1 = _layer_out(base, inp)
+    y2 = _layer_out(base, inp)
+    assert torch.equal(y1, y2), "run-to-run difference"
+    kp = MID.kp
+    split = MoELayer(inp, capacity=(MID.T * kp) // 3 + 5)
+    assert torch.equal(_layer_out(split, inp), y1), "capacity split changed the output"
+    perm = random_phi(MID.n_exp, MID.n_exp + 7, seed=11).tolist()
+    moved = MoELayer(inp, phi=perm, P=MID.n_exp + 7)
+    assert torch.equal(_layer_out(moved, inp), y1), "a different placement changed the output"
+
+
+def test_partial_phi_leaves_out_absent_experts():
+    say("partial placement map")
+    inp = gpu_inputs(MID)
+    layer = MoELayer(inp)
+    s = layer.shape
+    phi = list(range(MID.n_exp))
+    for e in (1, 4, 9):
+        phi[e] = -1
+    L = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    B.moe_router_logits(s, layer.X, layer.Wr, layer.bias, L)
+    B.moe_route_build(s, 0, s.T, L, phi, 0, layer.routes, layer.ws)
+    Y = inp.A.clone()
+    B.moe_expert_ffn(s, layer.X, Y, layer.routes, layer.arena, phi,
+                     B.MOE_FFN_EXPERTS | B.MOE_FFN_FINALIZE, layer.ws)
+    torch.cuda.synchronize()
+    orun = OracleRun(inp)
+    mask = np.isin(orun.idx, [1, 4, 9], invert=True).reshape(-1).astype(np.uint8)
+    ref = orun.route_map(phi, s.P)
+    check_descriptors(layer.routes, ref)
+    err = rel_err(np32(Y), orun.Y(route_mask=mask))
+    assert err <= TOL["bf16"], err
+
+
+def test_paged_equals_resident():
+    say("paged layer (P=16, G=8) vs resident")
+    cfg = CONFIGS["virt_olmoe_t512"]
+    inp = gpu_inputs(cfg)
+    res = MoELayer(inp)                 # all 64 experts resident
+    y_res = _layer_out(res, inp)
+    res.close()
+    paged = MoELayer(inp, paged=True)   # P = 16 slots, banks of 8
+    copy = torch.cuda.Stream()
+    Y = inp.A.clone()
+    paged.forward(Y, copy=copy)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, y_res), "paging changed the output"
+    y2 = inp.A.clone()
+    paged.forward(y2, copy=copy)        # the arena is reused by a second call
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y_res)
+    counts = np.bincount(paged.routes["topk_idx"].cpu().numpy().reshape(-1), minlength=cfg.E)
+    say(f"  experts with no routes: {int((counts == 0).sum())}")
+    orun = OracleRun(inp)
+    toks = sample_tokens(cfg.T, 48)
+    assert rel_err(np32(Y)[toks], orun.Y(tokens=toks)) <= TOL["bf16"]
+
+
+def test_edge_shapes():
+    say("edge shapes")
+    for T in (1, 77):
+        _check_layer(MID.with_(T=T, name=f"mid_T{T}"))
+    # an empty prompt is a no-op
+    cfg = MID.with_(T=0, name="mid_T0")
+    inp = make_inputs(MID.with_(T=0), device="cuda")
+    layer = MoELayer(inp)
+    Y = inp.A.clone()
+    layer.forward(Y)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, MID.d)
