@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Throughput of one routed-expert MoE layer on one MI355X.
+
+A step is one whole layer over one prompt, through the C ABI
+(moe_layer_prefill): fp32 router logits, top-k routing, the per-slot route
+map, gate/up + SwiGLU and down projections on bf16 MFMA, and the fixed-order
+combine into the fp32 accumulator. Inputs and weights are resident in HBM
+before timing starts; data is synthetic (seeded, the shapes of the models on
+the pages; no trained weights).
+
+Prints one JSON line: routed tokens/s (T / layer time), the % of the bf16
+MFMA peak the layer reaches on its algorithmic FLOPs, a roofline entry for
+the dominant kernel (the gate/up projection) timed with HIP events around
+its own launches inside the timed region, and the CPU oracle's throughput on
+a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload olmoe_t4096]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/s per MoE layer + % bf16 MFMA peak at T=4096 (1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+WORKLOAD_TEXT = {
+    "olmoe_t4096": "OLMoE-shaped MoE layer: T=4096 tokens, d=2048, E=64 experts, top-8 renormalised, "
+                   "SwiGLU f=1024, bf16 weights/activations, fp32 router and accumulator",
+    "olmoe_t1024": "OLMoE-shaped MoE layer: T=1024 tokens, d=2048, E=64 experts, top-8 renormalised, "
+                   "SwiGLU f=1024, bf16",
+    "dsv2lite_t4096": "DeepSeek-V2-Lite-shaped MoE layer: T=4096, d=2048, 64 routed experts top-6 "
+                      "(not renormalised) + 2 shared, SwiGLU f=1408, bf16",
+    "mixtral_t4096": "Mixtral-8x7B-shaped MoE layer: T=4096, d=4096, E=8, top-2 renormalised, SwiGLU "
+                     "f=14336, bf16",
+    "mixtral_t1024": "Mixtral-8x7B-shaped MoE layer: T=1024, d=4096, E=8, top-2, f=14336, bf16",
+    "mixtral_t256": "Mixtral-8x7B-shaped MoE layer: T=256, d=4096, E=8, top-2, f=14336, bf16",
+    "tiny_fp32": "tiny fp32 MoE layer: T=64, d=128, E=8, top-2, f=256",
+}
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("expert_gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "routed_expert_ffn_top_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, launch_flops: float):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"gate_up_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != gemm_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def torch_matmul_ceiling(torch, n=8192, reps=10) -> float:
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        a @ b
+    e.record()
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 * reps / (s.elapsed_time(e) / 1e3) / 1e12
+
+
+def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
+    """The CPU oracle (as it stands) on the same workload: routing for every
+    token, the expert FFN on a token sample sized to ~target_s seconds,
+    extrapolated to the whole layer."""
+    import numpy as np
+    from oracle import oracle as oracle_mod
+
+    orc = oracle_mod.get()
+    f32 = lambda t: t.detach().float().cpu().numpy()
+    X, Wr = f32(inp.X), f32(inp.Wr)
+    bias = None if inp.bias is None else f32(inp.bias)
+    Wg, Wu, Wd = f32(inp.Wg), f32(inp.Wu), f32(inp.Wd)
+    t0 = time.perf_counter()
+    L = orc.router_logits(X, Wr, bias)
+    idx, alpha = orc.topk(L, cfg.k, cfg.n_shared, cfg.renorm)
+    orc.route_map(idx, np.arange(cfg.n_exp, dtype=np.int32), cfg.n_exp)
+    t_route = time.perf_counter() - t0
+    probe = min(cfg.T, 16)
+    t1 = time.perf_counter()
+    orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, None, tokens=np.arange(probe))
+    per_tok = (time.perf_counter() - t1) / probe
+    n = int(min(cfg.T, max(probe, target_s / max(per_tok, 1e-9))))
+    rng = np.random.default_rng(5)
+    toks = np.sort(rng.choice(cfg.T, size=n, replace=False))
+    t2 = time.perf_counter()
+    orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, None, tokens=toks)
+    t_ffn = time.perf_counter() - t2
+    t_layer = t_route + t_ffn * cfg.T / n
+    return {"value": round(cfg.T / t_layer, 3), "unit": "tokens/s", "cores": orc.threads(),
+            "kind": "oracle",
+            "sample": f"router, top-k and route map for all {cfg.T} tokens ({t_route:.2f} s); expert FFN "
+                      f"for {n} sampled tokens ({t_ffn:.2f} s), extrapolated to T={cfg.T}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="olmoe_t4096", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true", help="skip the torch.matmul ceiling")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU (one MI355X); "
+                                   f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported"}))
+        return 2
+
+    import torch
+
+    from routed_expert_ffn_top_amd import binding as B
+    from routed_expert_ffn_top_amd.inputs import CONFIGS, make_inputs
+    from routed_expert_ffn_top_amd.layer import MoELayer
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 5}))
+        return 0
+
+    B.load()
+    cfg = CONFIGS[args.workload]
+    inp = make_inputs(cfg, device="cuda", residual=False)
+    layer = MoELayer(inp)
+    Y = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        layer.forward(Y)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    # timed region: K whole layers; the gate/up launches carry event pairs
+    B.moe_profile_begin("gate_up", K)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record()
+    for _ in range(K):
+        layer.forward(Y)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gate_up_ms = B.moe_profile_end("gate_up", K)
+    ms = start.elapsed_time(stop) / K
+
+    # per-kernel breakdown: a second pass with every kernel bracketed
+    names = ["router", "topk", "route_count", "route_scan", "route_place", "gate_up", "down", "combine"]
+    reps = min(K, 10)
+    for nme in names:
+        B.moe_profile_begin(nme, reps)
+    for _ in range(reps):
+        layer.forward(Y)
+    torch.cuda.synchronize()
+    breakdown = {}
+    for nme in names:
+        d = B.moe_profile_end(nme, reps)
+        breakdown[nme] = round(sum(d) / len(d), 4) if d else None
+
+    R = cfg.T * cfg.kp
+    flops_layer = 6.0 * R * cfg.d * cfg.f
+    gate_up_flops = 4.0 * R * cfg.d * cfg.f
+    down_flops = 2.0 * R * cfg.d * cfg.f
+    gu_avg = sum(gate_up_ms) / len(gate_up_ms)
+    achieved = gate_up_flops / (gu_avg / 1e3) / 1e12
+    traffic = read_traffic(args.workload, gate_up_flops)
+    tokens_s = cfg.T / (ms / 1e3)
+    ffn_ms = (breakdown["gate_up"] or 0) + (breakdown["down"] or 0)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; random-init, no checkpoint)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "T": cfg.T, "d": cfg.d, "E": cfg.E,
+                   "k": cfg.k, "n_shared": cfg.n_shared, "f": cfg.f, "slots": layer.shape.P,
+                   "router": "fp32 logits computed in the step", "parallelism": "single GPU"},
+        "routes_per_s": round(R / (ms / 1e3), 1),
+        "pct_bf16_peak_layer": round(100.0 * flops_layer / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "expert_ffn_tflops": round(flops_layer / (ffn_ms / 1e3) / 1e12, 1) if ffn_ms else None,
+        "pct_bf16_peak_expert_ffn": round(100.0 * flops_layer / (ffn_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2)
+        if ffn_ms else None,
+        "kernel_ms": breakdown,
+        "down_tflops": round(down_flops / (breakdown["down"] / 1e3) / 1e12, 1) if breakdown["down"] else None,
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "kernel": "gate_up (gathered X rows x packed gate/up slice, bf16 MFMA, SwiGLU epilogue)",
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "launch_ms_avg": round(gu_avg, 4),
+            "flops_per_launch": gate_up_flops,
+        },
+    }
+    if not args.no_context:
+        out["context"] = {"torch_matmul_bf16_8192_tflops": round(torch_matmul_ceiling(torch), 1)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, cfg)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

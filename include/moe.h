@@ -171,6 +171,8 @@ moe_status moe_device_errors(const moe_shape *shape, void *ws, size_t ws_bytes,
  *   W_r    device [d][E] fp32
  *   bias   device [E] fp32 or NULL (added after the product)
  *   logits device [T][E] fp32, output
+ * Requires E <= 64 (MOE_ERR_UNSUPPORTED otherwise; larger routers can pass
+ * logits to moe_route_build).
  * logits[t][e] = acc + bias[e], where acc is the fp32 fused multiply-add
  * chain over i = 0..d-1 in ascending order starting from 0: this fixes the
  * bits of every logit, so the top-k decision is reproducible.
@@ -322,6 +324,26 @@ moe_status arena_slot_info(const moe_arena *arena, int32_t slot,
  * lane layout is the hardware's.
  */
 moe_status moe_selftest_mfma_layout(float *out, moe_stream stream);
+
+/*
+ * Per-kernel timing. Kernel ids of the layer's launches: */
+#define MOE_KERNEL_ROUTER 1
+#define MOE_KERNEL_TOPK 2
+#define MOE_KERNEL_ROUTE_COUNT 3
+#define MOE_KERNEL_ROUTE_SCAN 4
+#define MOE_KERNEL_ROUTE_PLACE 5
+#define MOE_KERNEL_GATE_UP 6
+#define MOE_KERNEL_DOWN 7
+#define MOE_KERNEL_COMBINE 8
+#define MOE_KERNEL_COUNT 9
+/* moe_profile_begin arms timing of one kernel id for the next max_launches
+ * launches (process-wide): each such launch is bracketed by a pair of HIP
+ * events recorded on the launch's stream. moe_profile_end waits for those
+ * events, writes up to n per-launch durations in milliseconds to ms (host),
+ * stores the number of timed launches in *recorded and disarms. */
+moe_status moe_profile_begin(int32_t kernel, int32_t max_launches);
+moe_status moe_profile_end(int32_t kernel, float *ms, int32_t n,
+                           int32_t *recorded);
 
 #ifdef __cplusplus
 }

@@ -77,7 +77,12 @@ _SIGS = {
     "arena_phi": ([_VP, _VP, _I32], _I32),
     "arena_slot_info": ([_VP, _I32, _VP, _VP], _I32),
     "moe_selftest_mfma_layout": ([_VP, _VP], _I32),
+    "moe_profile_begin": ([_I32, _I32], _I32),
+    "moe_profile_end": ([_I32, _VP, _I32, _VP], _I32),
 }
+
+MOE_KERNEL = {"router": 1, "topk": 2, "route_count": 3, "route_scan": 4, "route_place": 5,
+              "gate_up": 6, "down": 7, "combine": 8}
 
 
 def lib_path() -> str:
@@ -317,3 +322,14 @@ class Arena:
             moe_pack_gate_up(self.shape, Wg[e], Wu[e], self.plane_gu[s], 1, 0, 0, stream)
             self.plane_d[s].copy_(Wd[e])
             arena_publish_slot(self, s, e, stream)
+
+
+def moe_profile_begin(kernel: str, max_launches: int):
+    _check(load().moe_profile_begin(MOE_KERNEL[kernel], max_launches))
+
+
+def moe_profile_end(kernel: str, n: int) -> list:
+    buf = (ctypes.c_float * n)()
+    rec = ctypes.c_int32(0)
+    _check(load().moe_profile_end(MOE_KERNEL[kernel], buf, n, ctypes.byref(rec)))
+    return [float(buf[i]) for i in range(min(n, rec.value))]

@@ -129,6 +129,40 @@ moe_status check_phi(const moe_shape *s, const int32_t *phi, PhiArg *out)
 template <typename T>
 T *ws_at(void *ws, size_t off) { return (T *)((char *)ws + off); }
 
+// Per-kernel launch timing (moe_profile_begin / moe_profile_end).
+struct KernelTimer {
+    std::vector<hipEvent_t> start, stop;
+    int armed = 0, next = 0;
+};
+std::mutex g_prof_mu;
+KernelTimer g_prof[MOE_KERNEL_COUNT];
+
+// Records the start event of the next timed launch of `kid`; returns the
+// slot index or -1. Cheap when nothing is armed.
+int prof_begin(int kid, hipStream_t st)
+{
+    KernelTimer &k = g_prof[kid];
+    if (!k.armed) return -1;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (k.next >= (int)k.start.size()) return -1;
+    const int i = k.next++;
+    (void)hipEventRecord(k.start[i], st);
+    return i;
+}
+
+void prof_end(int kid, int i, hipStream_t st)
+{
+    if (i >= 0) (void)hipEventRecord(g_prof[kid].stop[i], st);
+}
+
+#define TIMED(kid, st, expr)                 \
+    ([&]() {                                 \
+        const int _pi = prof_begin(kid, st); \
+        hipError_t _r = (expr);              \
+        prof_end(kid, _pi, st);              \
+        return _r;                           \
+    }())
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -274,7 +308,8 @@ moe_status route_build_impl(const moe_shape &s, const WsLayout &w, int t0, int n
     int32_t *done = ws_at<int32_t>(ws, w.done);
     int reset = (flags & MOE_ROUTE_RESET) ? 1 : 0;
     if (logits) {
-        HIP_TRY(launch_topk(s, t0, nt, logits, r.topk_idx, r.topk_w, done, st), "top-k launch");
+        HIP_TRY(TIMED(MOE_KERNEL_TOPK, st, launch_topk(s, t0, nt, logits, r.topk_idx, r.topk_w, done, st)),
+                "top-k launch");
         reset = 0;  // top-k cleared the marks of the range
     }
     const int64_t i0 = (int64_t)t0 * kp, n = (int64_t)nt * kp;
@@ -282,9 +317,14 @@ moe_status route_build_impl(const moe_shape &s, const WsLayout &w, int t0, int n
     int32_t *blk = ws_at<int32_t>(ws, w.blk);
     int32_t *rank = ws_at<int32_t>(ws, w.rank);
     int32_t *err = ws_at<int32_t>(ws, w.err);
-    HIP_TRY(launch_route_count(s, i0, n, r.topk_idx, phi, blk, rank, err, done, reset, st), "route count launch");
-    HIP_TRY(launch_route_scan(s, nblk, blk, r.slot_count, r.slot_offset, st), "route scan launch");
-    HIP_TRY(launch_route_place(s, i0, n, r.topk_idx, phi, blk, rank, r.rec_token, r.rec_route, r.route_pos, st),
+    HIP_TRY(TIMED(MOE_KERNEL_ROUTE_COUNT, st,
+                  launch_route_count(s, i0, n, r.topk_idx, phi, blk, rank, err, done, reset, st)),
+            "route count launch");
+    HIP_TRY(TIMED(MOE_KERNEL_ROUTE_SCAN, st, launch_route_scan(s, nblk, blk, r.slot_count, r.slot_offset, st)),
+            "route scan launch");
+    HIP_TRY(TIMED(MOE_KERNEL_ROUTE_PLACE, st,
+                  launch_route_place(s, i0, n, r.topk_idx, phi, blk, rank, r.rec_token, r.rec_route,
+                                     r.route_pos, st)),
             "route place launch");
     return MOE_OK;
 }
@@ -313,7 +353,7 @@ moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, co
     g.K = s.d;
     g.C = ws_at<char>(ws, w.H);
     g.ldc = s.f;
-    HIP_TRY(launch_gate_up(s, g, max_rows, simple, st), "gate/up launch");
+    HIP_TRY(TIMED(MOE_KERNEL_GATE_UP, st, launch_gate_up(s, g, max_rows, simple, st)), "gate/up launch");
     GemmArgs h = gemm_args(s, r, a);
     h.A = ws_at<char>(ws, w.H);
     h.lda = s.f;
@@ -324,7 +364,7 @@ moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, co
     h.C = ws_at<float>(ws, w.Yr);
     h.ldc = s.d;
     h.done = ws_at<int32_t>(ws, w.done);
-    HIP_TRY(launch_down(s, h, max_rows, simple, st), "down launch");
+    HIP_TRY(TIMED(MOE_KERNEL_DOWN, st, launch_down(s, h, max_rows, simple, st)), "down launch");
     return MOE_OK;
 }
 
@@ -381,7 +421,9 @@ moe_status moe_router_logits(const moe_shape *shape, const void *X, const float 
 {
     MOE_TRY(check_shape(shape));
     if (!X || !W_r || !logits) return fail(MOE_ERR_INVALID_ARG, "router: NULL pointer");
-    HIP_TRY(launch_router_logits(*shape, X, W_r, bias, logits, S(stream)), "router launch");
+    if (shape->E > 64) return fail(MOE_ERR_UNSUPPORTED, "the router kernel covers E <= 64");
+    HIP_TRY(TIMED(MOE_KERNEL_ROUTER, S(stream), launch_router_logits(*shape, X, W_r, bias, logits, S(stream))),
+            "router launch");
     return MOE_OK;
 }
 
@@ -432,7 +474,8 @@ moe_status moe_expert_ffn(const moe_shape *shape, const void *X, float *Y, const
     }
     if (flags & MOE_FFN_FINALIZE) {
         if (!Y || !aligned(Y, 16)) return fail(MOE_ERR_INVALID_ARG, "Y must be non-NULL and 16-byte aligned");
-        HIP_TRY(launch_combine(*shape, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), S(stream)),
+        HIP_TRY(TIMED(MOE_KERNEL_COMBINE, S(stream),
+                      launch_combine(*shape, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), S(stream))),
                 "combine launch");
     }
     return MOE_OK;
@@ -567,6 +610,39 @@ moe_status arena_slot_info(const moe_arena *a, int32_t slot, int32_t *state, int
     return MOE_OK;
 }
 
+moe_status moe_profile_begin(int32_t kernel, int32_t max_launches)
+{
+    if (kernel <= 0 || kernel >= MOE_KERNEL_COUNT || max_launches < 1 || max_launches > 100000)
+        return fail(MOE_ERR_INVALID_ARG, "profile: bad kernel id or count");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    KernelTimer &k = g_prof[kernel];
+    while ((int)k.start.size() < max_launches) {
+        hipEvent_t a, b;
+        HIP_TRY(hipEventCreate(&a), "hipEventCreate");
+        HIP_TRY(hipEventCreate(&b), "hipEventCreate");
+        k.start.push_back(a);
+        k.stop.push_back(b);
+    }
+    k.next = 0;
+    k.armed = 1;
+    return MOE_OK;
+}
+
+moe_status moe_profile_end(int32_t kernel, float *ms, int32_t n, int32_t *recorded)
+{
+    if (kernel <= 0 || kernel >= MOE_KERNEL_COUNT) return fail(MOE_ERR_INVALID_ARG, "profile: bad kernel id");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    KernelTimer &k = g_prof[kernel];
+    k.armed = 0;
+    if (recorded) *recorded = k.next;
+    for (int i = 0; i < k.next && i < n && ms; ++i) {
+        HIP_TRY(hipEventSynchronize(k.stop[i]), "hipEventSynchronize");
+        HIP_TRY(hipEventElapsedTime(&ms[i], k.start[i], k.stop[i]), "hipEventElapsedTime");
+    }
+    k.next = 0;
+    return MOE_OK;
+}
+
 moe_status moe_selftest_mfma_layout(float *out, moe_stream stream)
 {
     if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
@@ -586,6 +662,7 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
     MOE_TRY(check_ws(shape, ws, ws_bytes, &w));
     if (!X || !Y || !arena) return fail(MOE_ERR_INVALID_ARG, "layer: X, Y and arena are required");
     if (!W_r && !logits) return fail(MOE_ERR_INVALID_ARG, "layer: give W_r or logits");
+    if (W_r && shape->E > 64) return fail(MOE_ERR_UNSUPPORTED, "the router kernel covers E <= 64");
     if (!aligned(Y, 16) || (shape->dtype == MOE_DT_BF16 && !aligned(X, 16)))
         return fail(MOE_ERR_INVALID_ARG, "layer: X and Y must be 16-byte aligned");
     if ((host_gu == nullptr) != (host_d == nullptr))
@@ -599,7 +676,8 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
     const float *L = logits;
     if (W_r) {
         L = ws_at<float>(ws, w.logits);
-        HIP_TRY(launch_router_logits(s, X, W_r, bias, ws_at<float>(ws, w.logits), cs), "router launch");
+        HIP_TRY(TIMED(MOE_KERNEL_ROUTER, cs, launch_router_logits(s, X, W_r, bias, ws_at<float>(ws, w.logits), cs)),
+                "router launch");
     }
     std::vector<int32_t> phi(kMaxExp, -1);
     PhiArg pa;
@@ -620,7 +698,8 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
             MOE_TRY(experts_impl(s, w, X, *routes, arena, nt * kp, false, ws, cs));
         }
         MOE_TRY(arena_release_after(arena, phi.data(), cs));
-        HIP_TRY(launch_combine(s, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), cs), "combine launch");
+        HIP_TRY(TIMED(MOE_KERNEL_COMBINE, cs, launch_combine(s, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), cs)),
+                "combine launch");
         return MOE_OK;
     }
 
@@ -634,7 +713,9 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
     if ((int64_t)s.T * kp > s.capacity)
         return fail(MOE_ERR_CAPACITY, "paging needs capacity >= T*K' (%lld)", (long long)s.T * kp);
     const int G = arena->G, B = s.P / G;
-    HIP_TRY(launch_topk(s, 0, s.T, L, routes->topk_idx, routes->topk_w, ws_at<int32_t>(ws, w.done), cs), "top-k launch");
+    HIP_TRY(TIMED(MOE_KERNEL_TOPK, cs,
+                  launch_topk(s, 0, s.T, L, routes->topk_idx, routes->topk_w, ws_at<int32_t>(ws, w.done), cs)),
+            "top-k launch");
     HIP_TRY(launch_expert_hist(s, routes->topk_idx, (int64_t)s.T * kp, ws_at<int32_t>(ws, w.ecount), cs),
             "histogram launch");
     std::vector<int32_t> ecount(ne, 0);
@@ -669,7 +750,8 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
         MOE_TRY(experts_impl(s, w, X, *routes, arena, s.T * kp, false, ws, cs));
         MOE_TRY(arena_release_after(arena, phi.data(), cs));
     }
-    HIP_TRY(launch_combine(s, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), cs), "combine launch");
+    HIP_TRY(TIMED(MOE_KERNEL_COMBINE, cs, launch_combine(s, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), cs)),
+                "combine launch");
     return MOE_OK;
 }
 

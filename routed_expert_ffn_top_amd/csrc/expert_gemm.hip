@@ -150,8 +150,10 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma(GemmArgs a)
     if (!find_tile<BM, BN>(a, &ti)) return;
     const int slot = ti.slot, row0 = ti.row0, rows = ti.rows, n0 = ti.n0;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = __builtin_amdgcn_readfirstlane(wave / WN), wn = __builtin_amdgcn_readfirstlane(wave % WN);
     const int K = a.K, N = a.N;
+    // a wave whose rows all lie past the tile's valid rows does no MFMA work
+    const bool wave_active = wm * TM < __builtin_amdgcn_readfirstlane(rows);
 
     const uint16_t *aptr[CA];
     const uint16_t *bptr[CB];
@@ -213,24 +215,33 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma(GemmArgs a)
         }
         const uint16_t *As = &lds[cur][0];
         const uint16_t *Bs = &lds[cur][BM * LDK];
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8_t af[MI], bfr[NI];
-            const int koff = ks * 16 + (lane >> 5) * 8;
+        if (wave_active) {
+            // fragments of k16 step ks+1 are read while step ks's MFMAs run
+            bf16x8_t af[2][MI], bfr[2][NI];
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                af[i] = *(const bf16x8_t *)(As + (wm * TM + i * 32 + (lane & 31)) * LDK + koff);
+                af[0][i] = *(const bf16x8_t *)(As + (wm * TM + i * 32 + (lane & 31)) * LDK + (lane >> 5) * 8);
 #pragma unroll
             for (int j = 0; j < NI; ++j)
-                bfr[j] = *(const bf16x8_t *)(Bs + (wn * TN + j * 32 + (lane & 31)) * LDK + koff);
+                bfr[0][j] = *(const bf16x8_t *)(Bs + (wn * TN + j * 32 + (lane & 31)) * LDK + (lane >> 5) * 8);
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                if (wm * TM + i * 32 < rows) {
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                const int cs = ks & 1;
+                if (ks + 1 < BK / 16) {
+                    const int koff = (ks + 1) * 16 + (lane >> 5) * 8;
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+                        af[cs ^ 1][i] = *(const bf16x8_t *)(As + (wm * TM + i * 32 + (lane & 31)) * LDK + koff);
 #pragma unroll
                     for (int j = 0; j < NI; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],
-                                                                            0, 0, 0);
+                        bfr[cs ^ 1][j] = *(const bf16x8_t *)(Bs + (wn * TN + j * 32 + (lane & 31)) * LDK + koff);
                 }
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NI; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cs][i], bfr[cs][j], acc[i][j], 0,
+                                                                            0, 0);
             }
         }
         if (kt + 1 < nk) {
@@ -240,6 +251,229 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma(GemmArgs a)
             for (int c = 0; c < CB; ++c) *(u32x4_t *)(&lds[cur ^ 1][blds[c]]) = rb[c];
         }
         __syncthreads();
+    }
+
+    if (GATEUP) {
+        uint16_t *H = (uint16_t *)a.C;
+        const int fN = N / 2;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+            for (int q = 0; q < NI / 2; ++q) {
+                const int fcol = ((n0 + wn * TN) / 64 + q) * 32 + (lane & 31);
+                if (fcol >= fN) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (m < rows)
+                        H[(int64_t)(row0 + m) * a.ldc + fcol] =
+                            f32_to_bf16(silu_mul(acc[i][2 * q][r], acc[i][2 * q + 1][r]));
+                }
+            }
+        }
+    } else {
+        float *Yr = (float *)a.C;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                const int n = n0 + wn * TN + j * 32 + (lane & 31);
+                if (n >= N) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (m < rows) Yr[(int64_t)s_route[m] * a.ldc + n] = s_alpha[m] * acc[i][j][r];
+                }
+            }
+        }
+        if (n0 == 0)
+            for (int m = tid; m < rows; m += NT) a.done[s_route[m]] = 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel with direct global->LDS loads and a ring of NS stages.
+//
+// Tile BM x BN, K step 32 (one stage = BM + BN rows of 64 bytes), 8 waves in
+// a 4 x 2 grid, each wave BM/4 x BN/2 as 32x32x16 MFMA tiles. Operand tiles
+// are copied straight from global memory into LDS by global_load_lds_dwordx4
+// (16 bytes per lane; one instruction fills 1 KB = 16 rows of one stage), so
+// no registers hold staged data and NS-1 stages are in flight while one is
+// consumed. Rows are stored XOR-swizzled: the 16-byte chunk c of row r sits
+// at chunk position c ^ ((r >> 2) & 3). LDS serves a 16-byte-per-lane read
+// for 16 lanes per cycle across 64 banks; 16 consecutive rows at the same
+// chunk then land in 16 distinct 16-byte bank groups, so the MFMA fragment
+// reads are conflict-free (the DMA writes fill 1 KB contiguously). One
+// barrier per stage: after it, every wave's copies into
+// this stage have landed (each wave first waits on its own copies) and every
+// wave has finished reading the stage that the next copy overwrites.
+#define LDS_AS __attribute__((address_space(3)))
+#define GLOBAL_AS __attribute__((address_space(1)))
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at bits 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int BM, int BN, int NS, bool GATEUP>
+__global__ __launch_bounds__(512) void k_gemm_mfma_lds(GemmArgs a)
+{
+    constexpr int NT = 512, WM = 4, WN = 2;
+    constexpr int BK = 32, ROWB = 64;                 // bytes per LDS row (32 bf16)
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int MI = TM / 32, NI = TN / 32;
+    constexpr int STAGE = (BM + BN) * ROWB;           // bytes per stage
+    constexpr int AI = BM / 16 / 8, BI = BN / 16 / 8; // 1 KB copies per wave per stage
+    constexpr int LOADS = AI + BI;
+    static_assert(BM % 128 == 0 && BN % 128 == 0, "tile");
+    static_assert(!GATEUP || (TN % 64) == 0, "gate/up pairs need 64-column wave tiles");
+
+    __shared__ TileInfo ti;
+    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+    __shared__ int32_t s_route[GATEUP ? 1 : BM];
+    __shared__ float s_alpha[GATEUP ? 1 : BM];
+
+    if (!find_tile<BM, BN>(a, &ti)) return;
+    const int slot = ti.slot, row0 = ti.row0, n0 = ti.n0;
+    const int rows = __builtin_amdgcn_readfirstlane(ti.rows);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int K = a.K, N = a.N;
+    const bool wave_active = wm * TM < rows;
+
+    // copy sources: instruction j of this wave covers rows 16*(wave*AI + j)
+    // .. +15 of A (and likewise of B); lane -> row + l/4, chunk position l%4
+    const char *asrc[AI];
+    const char *bsrc[BI];
+    const int lr = lane >> 2, lp = lane & 3;
+#pragma unroll
+    for (int j = 0; j < AI; ++j) {
+        const int r = (wave * AI + j) * 16 + lr;
+        const int c = lp ^ ((r >> 2) & 3);
+        const int rr = min(r, rows - 1);
+        const int64_t arow = GATEUP ? (int64_t)a.rec_token[row0 + rr] : (int64_t)(row0 + rr);
+        asrc[j] = (const char *)a.A + (arow * a.lda) * 2 + c * 16;
+    }
+    const char *Bslot = (const char *)a.B + (int64_t)slot * a.slot_stride * 2;
+#pragma unroll
+    for (int j = 0; j < BI; ++j) {
+        const int r = (wave * BI + j) * 16 + lr;
+        const int c = lp ^ ((r >> 2) & 3);
+        const int n = min(n0 + r, N - 1);
+        bsrc[j] = Bslot + (int64_t)n * K * 2 + c * 16;
+    }
+    if (!GATEUP) {
+        for (int m = tid; m < BM; m += NT) {
+            const int rt = a.rec_route[row0 + min(m, rows - 1)];
+            s_route[m] = rt;
+            s_alpha[m] = a.topk_w[rt];
+        }
+    }
+
+    auto issue = [&](int kt) {
+        char *st = lds + (kt % NS) * STAGE;
+        const int kb = kt * BK * 2;
+#pragma unroll
+        for (int j = 0; j < AI; ++j)
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(asrc[j] + kb),
+                                             (LDS_AS void *)(st + (wave * AI + j) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < BI; ++j)
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(bsrc[j] + kb),
+                                             (LDS_AS void *)(st + BM * ROWB + (wave * BI + j) * 1024), 16, 0,
+                                             0);
+    };
+
+    f32x16_t acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // fragment addressing: row (lane & 31) of each 32-row tile, logical chunk
+    // 2*ks + (lane >> 5), stored at chunk ^ (((lane & 31) >> 2) & 3)
+    const int sw = ((lane & 31) >> 2) & 3;
+    const int foff[2] = {(lane & 31) * ROWB + ((0 + (lane >> 5)) ^ sw) * 16,
+                         (lane & 31) * ROWB + ((2 + (lane >> 5)) ^ sw) * 16};
+    bf16x8_t af[2][MI], bfr[2][NI];
+    auto read_frags = [&](int stage, int ks, int set) {
+        const char *As = lds + stage * STAGE + wm * TM * ROWB + foff[ks];
+        const char *Bs = lds + stage * STAGE + BM * ROWB + wn * TN * ROWB + foff[ks];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[set][i] = *(const bf16x8_t *)(As + i * 32 * ROWB);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) bfr[set][j] = *(const bf16x8_t *)(Bs + j * 32 * ROWB);
+    };
+    auto mfmas = [&](int set) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
+    };
+    // interleave: the (MI + NI) fragment reads of the next step are spread
+    // over the MI * NI MFMAs of this step
+    auto interleave = [&]() {
+#pragma unroll
+        for (int q = 0; q < MI + NI; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
+    };
+
+    // Invariant at the top of iteration kt: stage kt is complete and visible
+    // to every wave, and this wave holds stage kt's step-0 fragments in set 0.
+    // During iteration kt, stage kt+1 is made visible (own copies waited for,
+    // then the barrier), so that its step-0 fragments can be read while stage
+    // kt's last MFMAs run, and stage kt+NS-1 is requested into the slot of
+    // stage kt-1, which every wave finished before that barrier.
+    const int nk = K / BK;
+    static_assert(NS >= 3, "the ring needs at least 3 stages");
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+        if (p < nk) issue(p);
+    if (nk > 1)
+        wait_vmcnt<(NS - 2) * LOADS>();
+    else
+        wait_vmcnt<0>();
+    __syncthreads();
+    if (wave_active) read_frags(0, 0, 0);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const int stage = kt % NS;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            // own copies of stage kt+1 landed: only stages kt+2 .. remain
+            if (kt + 2 < nk)
+                wait_vmcnt<(NS - 3) * LOADS>();
+            else
+                wait_vmcnt<0>();
+            // A bare barrier: the stage's data is visible once every wave has
+            // waited on its own copies, and the slot refilled below was last
+            // read by fragment loads whose results fed MFMAs issued before
+            // this point, so no LDS counter needs draining here and the
+            // fragment reads of the previous step stay in flight.
+            __builtin_amdgcn_s_barrier();
+            if (kt + NS - 1 < nk) issue(kt + NS - 1);
+        }
+        if (wave_active) {
+            read_frags(stage, 1, 1);
+            mfmas(0);
+            interleave();
+            // next stage's step-0 fragments (on the last step this re-reads a
+            // resident stage; the values are not used)
+            read_frags((kt + 1) % NS, 0, 0);
+            mfmas(1);
+            interleave();
+        }
     }
 
     if (GATEUP) {
@@ -385,6 +619,15 @@ hipError_t launch_mfma(const GemmArgs &a, int max_rows, hipStream_t st)
     return hipGetLastError();
 }
 
+template <int BM, int BN, int NS, bool GATEUP>
+hipError_t launch_mfma_lds(const GemmArgs &a, int max_rows, hipStream_t st)
+{
+    const unsigned g = grid_bound(a, max_rows, BM, BN);
+    if (g == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, GATEUP>), dim3(g), dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+
 template <typename TE, bool GATEUP>
 hipError_t launch_simple(const GemmArgs &a, int max_rows, hipStream_t st)
 {
@@ -396,13 +639,28 @@ hipError_t launch_simple(const GemmArgs &a, int max_rows, hipStream_t st)
 
 }  // namespace
 
+// Kernel choice for the bf16 projections: the direct-to-LDS ring kernel
+// (tile rows, tile columns, stages), or with MOE_REG_STAGED the register-
+// staged double-buffer kernel (rows, columns, wave grid).
+#ifndef MOE_GU_TILE
+#define MOE_GU_TILE 256, 256, 4
+#endif
+#ifndef MOE_DN_TILE
+#define MOE_DN_TILE 256, 256, 4
+#endif
+#ifdef MOE_REG_STAGED
+#define MOE_LAUNCH_MFMA launch_mfma
+#else
+#define MOE_LAUNCH_MFMA launch_mfma_lds
+#endif
+
 hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
                           hipStream_t st)
 {
     if (max_rows == 0) return hipSuccess;
     if (s.dtype == MOE_DT_F32) return launch_simple<float, true>(a, max_rows, st);
     if (simple) return launch_simple<uint16_t, true>(a, max_rows, st);
-    return launch_mfma<128, 128, 2, 2, true>(a, max_rows, st);
+    return MOE_LAUNCH_MFMA<MOE_GU_TILE, true>(a, max_rows, st);
 }
 
 hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
@@ -411,7 +669,7 @@ hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool
     if (max_rows == 0) return hipSuccess;
     if (s.dtype == MOE_DT_F32) return launch_simple<float, false>(a, max_rows, st);
     if (simple) return launch_simple<uint16_t, false>(a, max_rows, st);
-    return launch_mfma<128, 128, 2, 2, false>(a, max_rows, st);
+    return MOE_LAUNCH_MFMA<MOE_DN_TILE, false>(a, max_rows, st);
 }
 
 }  // namespace moe

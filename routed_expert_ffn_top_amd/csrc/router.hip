@@ -31,9 +31,19 @@ template <>
 __device__ __forceinline__ float load_x<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
 
 constexpr int kRouterKC = 64;   // hidden-index slab per LDS pass
+constexpr int kXS = kRouterKC + 4;   // padded row stride (floats) of both slabs
 
-// blockDim = 256. EPAD = E rounded up to a power of two (<= 256);
-// groups = 256 / EPAD token groups, each thread does NTOK tokens.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// blockDim = 256. EPAD = E rounded up to a power of two (<= 64 here; larger
+// E uses several lanes' worth of rows); thread (g, e) owns expert e of NTOK
+// tokens g, g + groups, ... with groups = 256 / EPAD. Per 64-wide hidden slab
+// the workgroup stages X (as fp32, row per token) and W_r transposed (row per
+// expert) in LDS, double-buffered, with the next slab's global loads in
+// flight while the current one is used. Each thread reads 4 consecutive
+// hidden indices of its expert row and of each token row as 16-byte LDS
+// reads and applies the 4 fused multiply-adds in ascending order, so every
+// logit is exactly the sequential fp32 chain.
 template <typename TX, int NTOK>
 __global__ __launch_bounds__(256) void k_router_logits(const TX *__restrict__ X, int64_t ldx,
                                                        const float *__restrict__ Wr,
@@ -46,43 +56,92 @@ __global__ __launch_bounds__(256) void k_router_logits(const TX *__restrict__ X,
     const int tid = threadIdx.x;
     const int e = tid & (epad - 1);
     const int g = tid >> epad_log2;
-    const int tok_per_wg = groups * NTOK;
-    const int tbase = blockIdx.x * tok_per_wg;
+    const int tpw = groups * NTOK;           // tokens per workgroup
+    const int tbase = blockIdx.x * tpw;
 
-    // X slab: [tok_per_wg][KC + 1] (odd stride: different token rows sit in
-    // different banks); W slab: [KC][E].
     extern __shared__ float smem[];
+    // [2][tpw][kXS] token slabs, then [2][E][kXS] transposed weight slabs
     float *xs = smem;
-    float *ws = smem + tok_per_wg * (kRouterKC + 1);
+    float *ws = smem + 2 * tpw * kXS;
 
     float acc[NTOK];
 #pragma unroll
     for (int n = 0; n < NTOK; ++n) acc[n] = 0.0f;
 
-    for (int i0 = 0; i0 < d; i0 += kRouterKC) {
-        const int kc = min(kRouterKC, d - i0);
-        for (int q = tid; q < tok_per_wg * kRouterKC; q += 256) {
-            const int r = q / kRouterKC, c = q % kRouterKC;
-            const int t = tbase + r;
-            xs[r * (kRouterKC + 1) + c] =
-                (t < T && c < kc) ? load_x<TX>(X + (int64_t)t * ldx + i0 + c) : 0.0f;
-        }
-        for (int q = tid; q < kRouterKC * E; q += 256) {
-            const int r = q / E, c = q % E;
-            ws[q] = (r < kc) ? Wr[(int64_t)(i0 + r) * E + c] : 0.0f;
-        }
-        __syncthreads();
-        if (e < E) {
-            for (int i = 0; i < kc; ++i) {
-                const float w = ws[i * E + e];
+    const int nfull = d / kRouterKC;
+    // global -> register staging: each thread moves up to 4 X values and up
+    // to 16 W values per slab (tpw*64 <= 2048 and 64*E <= 4096 elements).
+    constexpr int XR = 8, WR = 16;
+    float xr[XR], wr[WR];
+    auto gload = [&](int c) {
+        const int i0 = c * kRouterKC;
 #pragma unroll
-                for (int n = 0; n < NTOK; ++n)
-                    acc[n] = __builtin_fmaf(xs[(g + n * groups) * (kRouterKC + 1) + i], w, acc[n]);
+        for (int q = 0; q < XR; ++q) {
+            const int id = q * 256 + tid;
+            const int r = id / kRouterKC, col = id % kRouterKC, t = tbase + r;
+            xr[q] = (r < tpw && t < T) ? load_x<TX>(X + (int64_t)t * ldx + i0 + col) : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < WR; ++q) {
+            const int id = q * 256 + tid;
+            const int r = id / E, col = id % E;
+            wr[q] = (r < kRouterKC) ? Wr[(int64_t)(i0 + r) * E + col] : 0.0f;
+        }
+    };
+    auto sstore = [&](int buf) {
+        float *xb = xs + buf * tpw * kXS;
+        float *wb = ws + buf * E * kXS;
+#pragma unroll
+        for (int q = 0; q < XR; ++q) {
+            const int id = q * 256 + tid;
+            const int r = id / kRouterKC, col = id % kRouterKC;
+            if (r < tpw) xb[r * kXS + col] = xr[q];
+        }
+#pragma unroll
+        for (int q = 0; q < WR; ++q) {
+            const int id = q * 256 + tid;
+            const int r = id / E, col = id % E;
+            if (r < kRouterKC) wb[col * kXS + r] = wr[q];
+        }
+    };
+
+    if (nfull > 0) {
+        gload(0);
+        sstore(0);
+    }
+    __syncthreads();
+    for (int c = 0; c < nfull; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < nfull) gload(c + 1);
+        if (e < E) {
+            const float *wrow = ws + buf * E * kXS + e * kXS;
+            const float *xb = xs + buf * tpw * kXS;
+#pragma unroll
+            for (int i = 0; i < kRouterKC; i += 4) {
+                const f32x4_t w4 = *(const f32x4_t *)(wrow + i);
+#pragma unroll
+                for (int n = 0; n < NTOK; ++n) {
+                    const f32x4_t x4 = *(const f32x4_t *)(xb + (g + n * groups) * kXS + i);
+                    acc[n] = __builtin_fmaf(x4.x, w4.x, acc[n]);
+                    acc[n] = __builtin_fmaf(x4.y, w4.y, acc[n]);
+                    acc[n] = __builtin_fmaf(x4.z, w4.z, acc[n]);
+                    acc[n] = __builtin_fmaf(x4.w, w4.w, acc[n]);
+                }
             }
         }
+        if (c + 1 < nfull) sstore(buf ^ 1);
         __syncthreads();
     }
+    // tail (d not a multiple of 64): straight from global memory, in order
     if (e < E) {
+        for (int i = nfull * kRouterKC; i < d; ++i) {
+            const float w = Wr[(int64_t)i * E + e];
+#pragma unroll
+            for (int n = 0; n < NTOK; ++n) {
+                const int t = tbase + g + n * groups;
+                if (t < T) acc[n] = __builtin_fmaf(load_x<TX>(X + (int64_t)t * ldx + i), w, acc[n]);
+            }
+        }
         const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
         for (int n = 0; n < NTOK; ++n) {
@@ -188,24 +247,25 @@ hipError_t launch_router_logits(const moe_shape &s, const void *X, const float *
                                 const float *bias, float *L, hipStream_t st)
 {
     if (s.T == 0) return hipSuccess;
-    int lg = 0;
+    int lg = 3;  // at least 8 expert lanes: at most 32 token groups per workgroup
     while ((1 << lg) < s.E) ++lg;
+    if (lg > 6) return hipErrorInvalidValue;  // E <= 64 (checked by the caller)
     const int groups = 256 >> lg;
     const bool many = s.E >= 32;
-    const int ntok = many ? 4 : 1;
-    const int tok_per_wg = groups * ntok;
-    const dim3 grid((s.T + tok_per_wg - 1) / tok_per_wg);
-    const size_t shmem = (size_t)(tok_per_wg * (kRouterKC + 1) + kRouterKC * s.E) * sizeof(float);
+    const int ntok = many ? 2 : 1;
+    const int tpw = groups * ntok;            // <= 256 / EPAD * 2 <= 32 tokens
+    const dim3 grid((s.T + tpw - 1) / tpw);
+    const size_t shmem = (size_t)2 * (tpw + s.E) * kXS * sizeof(float);
     if (s.dtype == MOE_DT_BF16) {
         if (many)
-            hipLaunchKernelGGL((k_router_logits<uint16_t, 4>), grid, dim3(256), shmem, st,
+            hipLaunchKernelGGL((k_router_logits<uint16_t, 2>), grid, dim3(256), shmem, st,
                                (const uint16_t *)X, s.ldx, Wr, bias, L, s.T, s.d, s.E, lg);
         else
             hipLaunchKernelGGL((k_router_logits<uint16_t, 1>), grid, dim3(256), shmem, st,
                                (const uint16_t *)X, s.ldx, Wr, bias, L, s.T, s.d, s.E, lg);
     } else {
         if (many)
-            hipLaunchKernelGGL((k_router_logits<float, 4>), grid, dim3(256), shmem, st,
+            hipLaunchKernelGGL((k_router_logits<float, 2>), grid, dim3(256), shmem, st,
                                (const float *)X, s.ldx, Wr, bias, L, s.T, s.d, s.E, lg);
         else
             hipLaunchKernelGGL((k_router_logits<float, 1>), grid, dim3(256), shmem, st,
