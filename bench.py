@@ -75,6 +75,75 @@ def read_traffic(workload: str, launch_flops: float):
         return None
 
 
+def _pmc_per_kernel(path: str, counter: str) -> dict:
+    """Average of one counter per dispatch, by kernel name, from a
+    rocprofv3 --pmc counter_collection.csv."""
+    import csv
+    tot, n = {}, {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            k = r["Kernel_Name"]
+            tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+            n[k] = n.get(k, 0) + 1
+    return {k: (tot[k] / n[k], n[k]) for k in tot}
+
+
+def summarize_pmc(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, out, command) -> None:
+    """HBM bytes per gate/up launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a plain 1 GiB
+    device copy (bench.py --copy-calibration)."""
+    def pick(d, key):
+        hits = {k: v for k, v in d.items() if key(k)}
+        if not hits:
+            raise SystemExit(f"no matching kernel in {list(d)[:5]}")
+        return max(hits.items(), key=lambda kv: kv[1][0])
+    is_gu = lambda k: "k_gemm" in k and "true>" in k
+    is_copy = lambda k: "elementwise" in k.lower() and "Mul" in k
+    gf_name, (gf, gfn) = pick(_pmc_per_kernel(fetch_csv, "FETCH_SIZE"), is_gu)
+    gw_name, (gw, gwn) = pick(_pmc_per_kernel(write_csv, "WRITE_SIZE"), is_gu)
+    cf_name, (cf, _) = pick(_pmc_per_kernel(calib_fetch_csv, "FETCH_SIZE"), is_copy)
+    cw_name, (cw, _) = pick(_pmc_per_kernel(calib_write_csv, "WRITE_SIZE"), is_copy)
+    copy_bytes = float(1 << 30)
+    kf, kw = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    fetch_b, write_b = gf * 1024.0 * kf, gw * 1024.0 * kw
+    with open(out, "w") as fh:
+        fh.write(f"# HBM traffic of the gate/up projection kernel, OLMoE-shaped layer T=4096\n")
+        fh.write(f"# command: {command}\n")
+        fh.write(f"# kernel: {gf_name[:120]}\n")
+        fh.write(f"# calibration kernel: {cf_name[:100]} (reads 1 GiB, writes 1 GiB)\n")
+        fh.write(f"kernel_source_hash: {gemm_source_hash()}\n")
+        fh.write(f"dispatches_fetch: {gfn}\ndispatches_write: {gwn}\n")
+        fh.write(f"fetch_kib_per_dispatch_raw: {gf:.1f}\nwrite_kib_per_dispatch_raw: {gw:.1f}\n")
+        fh.write(f"copy_fetch_kib_raw: {cf:.1f}\ncopy_write_kib_raw: {cw:.1f}\n")
+        fh.write(f"fetch_scale: {kf:.4f}\nwrite_scale: {kw:.4f}\n")
+        fh.write(f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}\nhbm_write_bytes_per_launch: {write_b:.0f}\n")
+        fh.write(f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}\n")
+    print(open(out).read())
+
+
+def summarize_stats(stats_csv, out, command) -> None:
+    """Markdown table of a rocprofv3 --stats kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    with open(out, "w") as fh:
+        fh.write("# rocprofv3 kernel statistics\n\n")
+        fh.write(f"Command: `{command}`\n\n")
+        fh.write("| kernel | calls | avg us | min us | max us | total % |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            name = r.get("Name") or r.get("KernelName") or "?"
+            short = name.replace("void ", "").replace("(anonymous namespace)::", "")
+            short = short[:short.rfind("(")] if short.endswith(")") and "(" in short else short
+            short = short[:90]
+            avg = float(r.get("AverageNs", 0)) / 1e3
+            mn = float(r.get("MinNs", 0)) / 1e3
+            mx = float(r.get("MaxNs", 0)) / 1e3
+            fh.write(f"| `{short}` | {r.get('Calls')} | {avg:.1f} | {mn:.1f} | {mx:.1f} | "
+                     f"{float(r.get('Percentage', 0)):.2f} |\n")
+    print(open(out).read())
+
+
 def torch_matmul_ceiling(torch, n=8192, reps=10) -> float:
     a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
     b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
@@ -120,8 +189,9 @@ def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
     t_layer = t_route + t_ffn * cfg.T / n
     return {"value": round(cfg.T / t_layer, 3), "unit": "tokens/s", "cores": orc.threads(),
             "kind": "oracle",
-            "sample": f"router, top-k and route map for all {cfg.T} tokens ({t_route:.2f} s); expert FFN "
-                      f"for {n} sampled tokens ({t_ffn:.2f} s), extrapolated to T={cfg.T}"}
+            "sample": (f"router, top-k and route map for all {cfg.T} tokens ({t_route:.2f} s); expert FFN "
+                       + (f"for all {n} tokens ({t_ffn:.2f} s): the whole layer" if n == cfg.T else
+                          f"for {n} sampled tokens ({t_ffn:.2f} s), extrapolated to T={cfg.T}"))}
 
 
 def main() -> int:
@@ -134,7 +204,17 @@ def main() -> int:
     ap.add_argument("--no-context", action="store_true", help="skip the torch.matmul ceiling")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT_MD"))
+    ap.add_argument("--summarize-pmc", nargs=5,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV", "CALIB_WRITE_CSV", "OUT"))
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats, args.command)
+        return 0
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.command)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -150,13 +230,14 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     if args.copy_calibration:
+        # an elementwise kernel that reads 1 GiB and writes 1 GiB
         n = 1 << 28
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 5}))
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
         return 0
 
     B.load()
