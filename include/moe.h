@@ -172,7 +172,8 @@ moe_status moe_device_errors(const moe_shape *shape, void *ws, size_t ws_bytes,
  *   bias   device [E] fp32 or NULL (added after the product)
  *   logits device [T][E] fp32, output
  * Requires E <= 64 (MOE_ERR_UNSUPPORTED otherwise; larger routers can pass
- * logits to moe_route_build).
+ * logits to moe_route_build), X and W_r 16-byte aligned, and for fp32 X
+ * ldx % 4 == 0.
  * logits[t][e] = acc + bias[e], where acc is the fp32 fused multiply-add
  * chain over i = 0..d-1 in ascending order starting from 0: this fixes the
  * bits of every logit, so the top-k decision is reproducible.

@@ -129,6 +129,17 @@ moe_status check_phi(const moe_shape *s, const int32_t *phi, PhiArg *out)
 template <typename T>
 T *ws_at(void *ws, size_t off) { return (T *)((char *)ws + off); }
 
+// The router copies 16-byte pieces of X rows and W_r straight into LDS.
+moe_status check_router_args(const moe_shape *s, const void *X, const float *W_r)
+{
+    if (s->E > 64) return fail(MOE_ERR_UNSUPPORTED, "the router kernel covers E <= 64");
+    if (!aligned(X, 16) || !aligned(W_r, 16))
+        return fail(MOE_ERR_INVALID_ARG, "router: X and W_r must be 16-byte aligned");
+    if (s->dtype == MOE_DT_F32 && (s->ldx % 4) != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "router: fp32 X needs ldx %% 4 == 0");
+    return MOE_OK;
+}
+
 // Per-kernel launch timing (moe_profile_begin / moe_profile_end).
 struct KernelTimer {
     std::vector<hipEvent_t> start, stop;
@@ -421,7 +432,7 @@ moe_status moe_router_logits(const moe_shape *shape, const void *X, const float 
 {
     MOE_TRY(check_shape(shape));
     if (!X || !W_r || !logits) return fail(MOE_ERR_INVALID_ARG, "router: NULL pointer");
-    if (shape->E > 64) return fail(MOE_ERR_UNSUPPORTED, "the router kernel covers E <= 64");
+    MOE_TRY(check_router_args(shape, X, W_r));
     HIP_TRY(TIMED(MOE_KERNEL_ROUTER, S(stream), launch_router_logits(*shape, X, W_r, bias, logits, S(stream))),
             "router launch");
     return MOE_OK;
@@ -662,7 +673,7 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
     MOE_TRY(check_ws(shape, ws, ws_bytes, &w));
     if (!X || !Y || !arena) return fail(MOE_ERR_INVALID_ARG, "layer: X, Y and arena are required");
     if (!W_r && !logits) return fail(MOE_ERR_INVALID_ARG, "layer: give W_r or logits");
-    if (W_r && shape->E > 64) return fail(MOE_ERR_UNSUPPORTED, "the router kernel covers E <= 64");
+    if (W_r) MOE_TRY(check_router_args(shape, X, W_r));
     if (!aligned(Y, 16) || (shape->dtype == MOE_DT_BF16 && !aligned(X, 16)))
         return fail(MOE_ERR_INVALID_ARG, "layer: X and Y must be 16-byte aligned");
     if ((host_gu == nullptr) != (host_d == nullptr))

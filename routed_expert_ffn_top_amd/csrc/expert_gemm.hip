@@ -21,6 +21,8 @@
 // gathered rows). Workgroup ids are dealt round-robin to the 8 XCDs, so the
 // logical tile index is remapped to give each XCD one contiguous range of
 // tiles: the sharing happens in that XCD's own L2.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -122,6 +124,14 @@ template <>
 __device__ __forceinline__ void st_from_f32<uint16_t>(uint16_t *p, float v) { *p = f32_to_bf16(v); }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// SiLU(g) * u with the hardware exp2 and reciprocal (about 1 ulp each); used
+// where the result is rounded to bf16.
+__device__ __forceinline__ float silu_mul_fast(float g, float u)
+{
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel. WM x WN waves; each wave computes a (BM/WM) x (BN/WN)
@@ -319,62 +329,115 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int BM, int BN, int NS, bool GATEUP>
-__global__ __launch_bounds__(512) void k_gemm_mfma_lds(GemmArgs a)
+template <int BM, int BN, int NS, int WM, int WN, bool GATEUP>
+__global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
 {
-    constexpr int NT = 512, WM = 4, WN = 2;
-    constexpr int BK = 32, ROWB = 64;                 // bytes per LDS row (32 bf16)
+    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int BK = 32, ROWB = 64;                   // bytes per LDS row (32 bf16)
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MI = TM / 32, NI = TN / 32;
-    constexpr int STAGE = (BM + BN) * ROWB;           // bytes per stage
-    constexpr int AI = BM / 16 / 8, BI = BN / 16 / 8; // 1 KB copies per wave per stage
+    constexpr int STAGE = (BM + BN) * ROWB;             // bytes per stage
+    constexpr int AI = BM / 16 / NW, BI = BN / 16 / NW; // 1 KB copies per wave per stage
     constexpr int LOADS = AI + BI;
-    static_assert(BM % 128 == 0 && BN % 128 == 0, "tile");
+    static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0 && MI >= 1 && NI >= 1, "tile");
     static_assert(!GATEUP || (TN % 64) == 0, "gate/up pairs need 64-column wave tiles");
+    static_assert(NS >= 3, "the ring needs at least 3 stages");
 
-    __shared__ TileInfo ti;
     __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
-    __shared__ int32_t s_route[GATEUP ? 1 : BM];
-    __shared__ float s_alpha[GATEUP ? 1 : BM];
+    __shared__ int32_t s_route[2][GATEUP ? 1 : BM];   // by tile parity
+    __shared__ float s_alpha[2][GATEUP ? 1 : BM];
+    __shared__ int32_t s_tpref[kMaxExp + 1];           // first logical tile of each slot
+    __shared__ int32_t s_off[kMaxExp + 1];
 
-    if (!find_tile<BM, BN>(a, &ti)) return;
-    const int slot = ti.slot, row0 = ti.row0, n0 = ti.n0;
-    const int rows = __builtin_amdgcn_readfirstlane(ti.rows);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int K = a.K, N = a.N;
-    const bool wave_active = wm * TM < rows;
+    const int P = a.P;
+    const int ntn = (N + BN - 1) / BN;
+
+    // Tiles of slot s: ceil(count_s / BM) row blocks x ntn column blocks,
+    // numbered slot by slot, column block major, row block minor.
+    if (tid < 64) {
+        int run = 0;
+        for (int s0 = 0; s0 < P; s0 += 64) {
+            const int s = s0 + lane;
+            const int off = s < P ? a.slot_offset[s] : 0;
+            const int cnt = s < P ? a.slot_offset[s + 1] - off : 0;
+            const int w = (cnt + BM - 1) / BM * ntn;
+            const int inc = wave_incl_scan(w, lane);
+            if (s < P) {
+                s_tpref[s] = run + inc - w;
+                s_off[s] = off;
+            }
+            run += __shfl(inc, 63, 64);
+        }
+        if (lane == 0) {
+            s_tpref[P] = run;
+            s_off[P] = a.slot_offset[P];
+        }
+    }
+    __syncthreads();
+    const int total = s_tpref[P];
+    // The workgroups on XCD x = blockIdx % 8 walk one contiguous range of
+    // logical tiles together, one tile each per round, so neighbouring tiles
+    // (same weight tile, or same gathered rows) run at the same time there.
+    const int xcd = blockIdx.x % kXcd, li = blockIdx.x / kXcd;
+    const int nwg = ((int)gridDim.x - xcd + kXcd - 1) / kXcd;
+    const int qx = total / kXcd, rx = total % kXcd;
+    const int cnt_x = qx + (xcd < rx ? 1 : 0), start_x = xcd * qx + min(xcd, rx);
+    if (li >= cnt_x) return;
+
+    auto decode = [&](int L) -> TileInfo {
+        int lo = 0, hi = P - 1;  // last slot whose first tile is <= L (skips empty slots)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_tpref[mid] <= L) lo = mid; else hi = mid - 1;
+        }
+        const int cnt_s = s_off[lo + 1] - s_off[lo];
+        const int mt = (cnt_s + BM - 1) / BM;
+        const int local = L - s_tpref[lo];
+        const int ml = local % mt;
+        TileInfo t;
+        t.slot = lo;
+        t.row0 = s_off[lo] + ml * BM;
+        t.rows = __builtin_amdgcn_readfirstlane(min(BM, cnt_s - ml * BM));
+        t.n0 = (local / mt) * BN;
+        return t;
+    };
 
     // copy sources: instruction j of this wave covers rows 16*(wave*AI + j)
     // .. +15 of A (and likewise of B); lane -> row + l/4, chunk position l%4
     const char *asrc[AI];
     const char *bsrc[BI];
     const int lr = lane >> 2, lp = lane & 3;
+    auto set_sources = [&](const TileInfo &t) {
 #pragma unroll
-    for (int j = 0; j < AI; ++j) {
-        const int r = (wave * AI + j) * 16 + lr;
-        const int c = lp ^ ((r >> 2) & 3);
-        const int rr = min(r, rows - 1);
-        const int64_t arow = GATEUP ? (int64_t)a.rec_token[row0 + rr] : (int64_t)(row0 + rr);
-        asrc[j] = (const char *)a.A + (arow * a.lda) * 2 + c * 16;
-    }
-    const char *Bslot = (const char *)a.B + (int64_t)slot * a.slot_stride * 2;
-#pragma unroll
-    for (int j = 0; j < BI; ++j) {
-        const int r = (wave * BI + j) * 16 + lr;
-        const int c = lp ^ ((r >> 2) & 3);
-        const int n = min(n0 + r, N - 1);
-        bsrc[j] = Bslot + (int64_t)n * K * 2 + c * 16;
-    }
-    if (!GATEUP) {
-        for (int m = tid; m < BM; m += NT) {
-            const int rt = a.rec_route[row0 + min(m, rows - 1)];
-            s_route[m] = rt;
-            s_alpha[m] = a.topk_w[rt];
+        for (int j = 0; j < AI; ++j) {
+            const int r = (wave * AI + j) * 16 + lr;
+            const int c = lp ^ ((r >> 2) & 3);
+            const int rr = min(r, t.rows - 1);
+            const int64_t arow = GATEUP ? (int64_t)a.rec_token[t.row0 + rr] : (int64_t)(t.row0 + rr);
+            asrc[j] = (const char *)a.A + (arow * a.lda) * 2 + c * 16;
         }
-    }
-
+        const char *Bslot = (const char *)a.B + (int64_t)t.slot * a.slot_stride * 2;
+#pragma unroll
+        for (int j = 0; j < BI; ++j) {
+            const int r = (wave * BI + j) * 16 + lr;
+            const int c = lp ^ ((r >> 2) & 3);
+            const int n = min(t.n0 + r, N - 1);
+            bsrc[j] = Bslot + (int64_t)n * K * 2 + c * 16;
+        }
+    };
+    auto load_routes = [&](const TileInfo &t, int par) {
+        if (!GATEUP) {
+            for (int m = tid; m < BM; m += NT) {
+                const int rt = a.rec_route[t.row0 + min(m, t.rows - 1)];
+                s_route[par][m] = rt;
+                s_alpha[par][m] = a.topk_w[rt];
+            }
+        }
+    };
     auto issue = [&](int kt) {
         char *st = lds + (kt % NS) * STAGE;
         const int kb = kt * BK * 2;
@@ -389,19 +452,12 @@ __global__ __launch_bounds__(512) void k_gemm_mfma_lds(GemmArgs a)
                                              0);
     };
 
-    f32x16_t acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
     // fragment addressing: row (lane & 31) of each 32-row tile, logical chunk
     // 2*ks + (lane >> 5), stored at chunk ^ (((lane & 31) >> 2) & 3)
     const int sw = ((lane & 31) >> 2) & 3;
     const int foff[2] = {(lane & 31) * ROWB + ((0 + (lane >> 5)) ^ sw) * 16,
                          (lane & 31) * ROWB + ((2 + (lane >> 5)) ^ sw) * 16};
+    f32x16_t acc[MI][NI];
     bf16x8_t af[2][MI], bfr[2][NI];
     auto read_frags = [&](int stage, int ks, int set) {
         const char *As = lds + stage * STAGE + wm * TM * ROWB + foff[ks];
@@ -411,12 +467,14 @@ __global__ __launch_bounds__(512) void k_gemm_mfma_lds(GemmArgs a)
 #pragma unroll
         for (int j = 0; j < NI; ++j) bfr[set][j] = *(const bf16x8_t *)(Bs + j * 32 * ROWB);
     };
+    // B is the first MFMA operand, so the accumulator tile is transposed (see
+    // the epilogue)
     auto mfmas = [&](int set) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
     };
     // interleave: the (MI + NI) fragment reads of the next step are spread
     // over the MI * NI MFMAs of this step
@@ -429,88 +487,141 @@ __global__ __launch_bounds__(512) void k_gemm_mfma_lds(GemmArgs a)
         __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
     };
 
-    // Invariant at the top of iteration kt: stage kt is complete and visible
-    // to every wave, and this wave holds stage kt's step-0 fragments in set 0.
-    // During iteration kt, stage kt+1 is made visible (own copies waited for,
-    // then the barrier), so that its step-0 fragments can be read while stage
-    // kt's last MFMAs run, and stage kt+NS-1 is requested into the slot of
-    // stage kt-1, which every wave finished before that barrier.
     const int nk = K / BK;
-    static_assert(NS >= 3, "the ring needs at least 3 stages");
+    int tl = li, par = 0;
+    TileInfo cur = decode(start_x + tl);
+    set_sources(cur);
+    load_routes(cur, 0);
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
         if (p < nk) issue(p);
-    if (nk > 1)
-        wait_vmcnt<(NS - 2) * LOADS>();
-    else
-        wait_vmcnt<0>();
-    __syncthreads();
-    if (wave_active) read_frags(0, 0, 0);
 
-    for (int kt = 0; kt < nk; ++kt) {
-        const int stage = kt % NS;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            // own copies of stage kt+1 landed: only stages kt+2 .. remain
-            if (kt + 2 < nk)
-                wait_vmcnt<(NS - 3) * LOADS>();
-            else
-                wait_vmcnt<0>();
-            // A bare barrier: the stage's data is visible once every wave has
-            // waited on its own copies, and the slot refilled below was last
-            // read by fragment loads whose results fed MFMAs issued before
-            // this point, so no LDS counter needs draining here and the
-            // fragment reads of the previous step stay in flight.
-            __builtin_amdgcn_s_barrier();
-            if (kt + NS - 1 < nk) issue(kt + NS - 1);
-        }
-        if (wave_active) {
-            read_frags(stage, 1, 1);
-            mfmas(0);
-            interleave();
-            // next stage's step-0 fragments (on the last step this re-reads a
-            // resident stage; the values are not used)
-            read_frags((kt + 1) % NS, 0, 0);
-            mfmas(1);
-            interleave();
-        }
-    }
+    for (;;) {
+        const bool wave_active = wm * TM < cur.rows;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    if (GATEUP) {
-        uint16_t *H = (uint16_t *)a.C;
-        const int fN = N / 2;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-            for (int q = 0; q < NI / 2; ++q) {
-                const int fcol = ((n0 + wn * TN) / 64 + q) * 32 + (lane & 31);
-                if (fcol >= fN) continue;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (m < rows)
-                        H[(int64_t)(row0 + m) * a.ldc + fcol] =
-                            f32_to_bf16(silu_mul(acc[i][2 * q][r], acc[i][2 * q + 1][r]));
-                }
+        // Stage 0 of this tile is complete and visible. Loads return in
+        // order, so at most the later stages' copies remain once this wave
+        // has <= (NS-2)*LOADS memory operations outstanding, even with the
+        // previous tile's output stores still in flight.
+        if (nk > 1)
+            wait_vmcnt<(NS - 2) * LOADS>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+        if (wave_active) read_frags(0, 0, 0);
+
+        // Invariant at the top of step kt: stage kt is complete and visible
+        // to every wave, and this wave holds stage kt's step-0 fragments in
+        // set 0. During step kt, stage kt+1 is made visible (own copies
+        // waited for, then a barrier), so that its step-0 fragments can be
+        // read while stage kt's last MFMAs run, and stage kt+NS-1 is
+        // requested into the slot of stage kt-1, which every wave finished
+        // before that barrier.
+        for (int kt = 0; kt < nk; ++kt) {
+            const int stage = kt % NS;
+            const bool more = kt + 1 < nk;
+            if (more) {
+                if (kt + 2 < nk)
+                    wait_vmcnt<(NS - 3) * LOADS>();
+                else
+                    wait_vmcnt<0>();
+                // A bare barrier: the stage's data is visible once every wave
+                // has waited on its own copies, and the slot refilled below was
+                // last read by fragment loads whose results fed MFMAs issued
+                // before this point, so no LDS counter needs draining here.
+                __builtin_amdgcn_s_barrier();
+                if (kt + NS - 1 < nk) issue(kt + NS - 1);
+            }
+            if (wave_active) {
+                read_frags(stage, 1, 1);
+                mfmas(0);
+                interleave();
+                // next stage's step-0 fragments (on the last step this re-reads
+                // a resident stage; the values are not used)
+                read_frags((kt + 1) % NS, 0, 0);
+                mfmas(1);
+                interleave();
             }
         }
-    } else {
-        float *Yr = (float *)a.C;
+
+        // Start the next tile's copies before this tile's epilogue, which
+        // works from registers: once every wave is past this barrier nothing
+        // reads the ring any more.
+        const int tn = tl + nwg;
+        const bool has_next = tn < cnt_x;
+        TileInfo nxt = cur;
+        if (has_next) {
+            nxt = decode(start_x + tn);
+            __syncthreads();
+            set_sources(nxt);
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
+            for (int p = 0; p < NS - 1; ++p)
+                if (p < nk) issue(p);
+            load_routes(nxt, par ^ 1);  // the other parity: last read two tiles ago
+        }
+
+        // With B as the first MFMA operand the result tile is transposed: lane
+        // l holds row (l % 32) of its 32-row block and, in register group g
+        // (r / 4), the 4 consecutive columns 8g + 4*(l / 32) .. +3, so each
+        // lane stores 4 adjacent outputs with one vector store.
+        if (GATEUP) {
+            uint16_t *H = (uint16_t *)a.C;
+            const int fN = N / 2;
 #pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int n = n0 + wn * TN + j * 32 + (lane & 31);
-                if (n >= N) continue;
+            for (int i = 0; i < MI; ++i) {
+                const int m = wm * TM + i * 32 + (lane & 31);
+                if (m >= cur.rows) continue;
+                uint16_t *hrow = H + (int64_t)(cur.row0 + m) * a.ldc;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (m < rows) Yr[(int64_t)s_route[m] * a.ldc + n] = s_alpha[m] * acc[i][j][r];
+                for (int q = 0; q < NI / 2; ++q) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int f0 = ((cur.n0 + wn * TN) / 64 + q) * 32 + 8 * g + 4 * (lane >> 5);
+                        if (f0 >= fN) continue;
+                        uint32_t w[2];
+#pragma unroll
+                        for (int c = 0; c < 4; c += 2) {
+                            const float h0 = silu_mul_fast(acc[i][2 * q][4 * g + c], acc[i][2 * q + 1][4 * g + c]);
+                            const float h1 =
+                                silu_mul_fast(acc[i][2 * q][4 * g + c + 1], acc[i][2 * q + 1][4 * g + c + 1]);
+                            w[c / 2] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
+                        }
+                        *(uint2 *)(hrow + f0) = make_uint2(w[0], w[1]);
+                    }
                 }
             }
+        } else {
+            float *Yr = (float *)a.C;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const int m = wm * TM + i * 32 + (lane & 31);
+                if (m >= cur.rows) continue;
+                float *yrow = Yr + (int64_t)s_route[par][m] * a.ldc;
+                const float al = s_alpha[par][m];
+#pragma unroll
+                for (int j = 0; j < NI; ++j) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int n = cur.n0 + wn * TN + j * 32 + 8 * g + 4 * (lane >> 5);
+                        if (n >= N) continue;
+                        *(float4 *)(yrow + n) = make_float4(al * acc[i][j][4 * g], al * acc[i][j][4 * g + 1],
+                                                            al * acc[i][j][4 * g + 2], al * acc[i][j][4 * g + 3]);
+                    }
+                }
+            }
+            if (cur.n0 == 0)
+                for (int m = tid; m < cur.rows; m += NT) a.done[s_route[par][m]] = 1;
         }
-        if (n0 == 0)
-            for (int m = tid; m < rows; m += NT) a.done[s_route[m]] = 1;
+        if (!has_next) break;
+        cur = nxt;
+        tl = tn;
+        par ^= 1;
     }
 }
 
@@ -619,12 +730,26 @@ hipError_t launch_mfma(const GemmArgs &a, int max_rows, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int BM, int BN, int NS, bool GATEUP>
+inline int device_cus()
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
+
+template <int BM, int BN, int NS, int WM, int WN, bool GATEUP>
 hipError_t launch_mfma_lds(const GemmArgs &a, int max_rows, hipStream_t st)
 {
-    const unsigned g = grid_bound(a, max_rows, BM, BN);
+    // one persistent workgroup per compute unit (the LDS ring fills one CU),
+    // never more than there can be tiles
+    const unsigned g = std::min<unsigned>(grid_bound(a, max_rows, BM, BN), (unsigned)device_cus());
     if (g == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, GATEUP>), dim3(g), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP>), dim3(g), dim3(WM * WN * 64), 0, st, a);
     return hipGetLastError();
 }
 
@@ -640,13 +765,14 @@ hipError_t launch_simple(const GemmArgs &a, int max_rows, hipStream_t st)
 }  // namespace
 
 // Kernel choice for the bf16 projections: the direct-to-LDS ring kernel
-// (tile rows, tile columns, stages), or with MOE_REG_STAGED the register-
+// (tile rows, tile columns, stages, wave rows, wave columns), or with
+// MOE_REG_STAGED the register-
 // staged double-buffer kernel (rows, columns, wave grid).
 #ifndef MOE_GU_TILE
-#define MOE_GU_TILE 256, 256, 4
+#define MOE_GU_TILE 256, 256, 4, 4, 2
 #endif
 #ifndef MOE_DN_TILE
-#define MOE_DN_TILE 256, 256, 4
+#define MOE_DN_TILE 256, 256, 4, 4, 2
 #endif
 #ifdef MOE_REG_STAGED
 #define MOE_LAUNCH_MFMA launch_mfma
