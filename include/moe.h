@@ -168,12 +168,12 @@ moe_status moe_device_errors(const moe_shape *shape, void *ws, size_t ws_bytes,
 /*
  * Router logits, the input of top-k routing (section 2.2).
  *   X      device [T][ldx] dtype
- *   W_r    device [d][E] fp32
+ *   W_r    device [E][d] fp32 (row e holds expert e's weights over the
+ *          hidden index: the layout of a linear layer's weight d -> E)
  *   bias   device [E] fp32 or NULL (added after the product)
  *   logits device [T][E] fp32, output
- * Requires E <= 64 (MOE_ERR_UNSUPPORTED otherwise; larger routers can pass
- * logits to moe_route_build), X and W_r 16-byte aligned, and for fp32 X
- * ldx % 4 == 0.
+ * Requires X 16-byte aligned, W_r 4-byte aligned, and for fp32 X
+ * ldx % 4 == 0 (bf16 X already needs ldx % 8 == 0).
  * logits[t][e] = acc + bias[e], where acc is the fp32 fused multiply-add
  * chain over i = 0..d-1 in ascending order starting from 0: this fixes the
  * bits of every logit, so the top-k decision is reproducible.

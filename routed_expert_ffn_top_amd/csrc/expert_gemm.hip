@@ -467,14 +467,12 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
 #pragma unroll
         for (int j = 0; j < NI; ++j) bfr[set][j] = *(const bf16x8_t *)(Bs + j * 32 * ROWB);
     };
-    // B is the first MFMA operand, so the accumulator tile is transposed (see
-    // the epilogue)
     auto mfmas = [&](int set) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
     };
     // interleave: the (MI + NI) fragment reads of the next step are spread
     // over the MI * NI MFMAs of this step
@@ -566,33 +564,33 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
             load_routes(nxt, par ^ 1);  // the other parity: last read two tiles ago
         }
 
-        // With B as the first MFMA operand the result tile is transposed: lane
-        // l holds row (l % 32) of its 32-row block and, in register group g
-        // (r / 4), the 4 consecutive columns 8g + 4*(l / 32) .. +3, so each
-        // lane stores 4 adjacent outputs with one vector store.
+        // Result layout: register r of lane l holds row 8*(r/4) + 4*(l/32) +
+        // r%4 and column l%32 of its 32x32 block. Registers r and r+1 (r even)
+        // are rows R and R+1; adjacent lanes swap one of the two values (a DPP
+        // lane swap), so that the even lane holds columns (c, c+1) of row R
+        // and the odd lane the same columns of row R+1. Each store instruction
+        // then writes four whole 64-byte (bf16) or 128-byte (fp32) row
+        // segments.
+        const bool even = (lane & 1) == 0;
+        const int cpair = (lane & 31) & ~1;
         if (GATEUP) {
             uint16_t *H = (uint16_t *)a.C;
             const int fN = N / 2;
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
-                const int m = wm * TM + i * 32 + (lane & 31);
-                if (m >= cur.rows) continue;
-                uint16_t *hrow = H + (int64_t)(cur.row0 + m) * a.ldc;
 #pragma unroll
-                for (int q = 0; q < NI / 2; ++q) {
+                for (int r = 0; r < 16; r += 2) {
+                    const int m = wm * TM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3) + (even ? 0 : 1);
+                    uint16_t *hrow = H + (int64_t)(cur.row0 + min(m, cur.rows - 1)) * a.ldc;
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int f0 = ((cur.n0 + wn * TN) / 64 + q) * 32 + 8 * g + 4 * (lane >> 5);
-                        if (f0 >= fN) continue;
-                        uint32_t w[2];
-#pragma unroll
-                        for (int c = 0; c < 4; c += 2) {
-                            const float h0 = silu_mul_fast(acc[i][2 * q][4 * g + c], acc[i][2 * q + 1][4 * g + c]);
-                            const float h1 =
-                                silu_mul_fast(acc[i][2 * q][4 * g + c + 1], acc[i][2 * q + 1][4 * g + c + 1]);
-                            w[c / 2] = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
-                        }
-                        *(uint2 *)(hrow + f0) = make_uint2(w[0], w[1]);
+                    for (int q = 0; q < NI / 2; ++q) {
+                        const uint32_t h0 = f32_to_bf16(silu_mul_fast(acc[i][2 * q][r], acc[i][2 * q + 1][r]));
+                        const uint32_t h1 =
+                            f32_to_bf16(silu_mul_fast(acc[i][2 * q][r + 1], acc[i][2 * q + 1][r + 1]));
+                        const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)(even ? h1 : h0), 0xB1, 0xF, 0xF, false);
+                        const uint32_t packed = even ? (h0 | (y << 16)) : (y | (h1 << 16));
+                        const int fcol = ((cur.n0 + wn * TN) / 64 + q) * 32 + cpair;
+                        if (m < cur.rows && fcol < fN) *(uint32_t *)(hrow + fcol) = packed;
                     }
                 }
             }
@@ -600,18 +598,20 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
             float *Yr = (float *)a.C;
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
-                const int m = wm * TM + i * 32 + (lane & 31);
-                if (m >= cur.rows) continue;
-                float *yrow = Yr + (int64_t)s_route[par][m] * a.ldc;
-                const float al = s_alpha[par][m];
 #pragma unroll
-                for (int j = 0; j < NI; ++j) {
+                for (int r = 0; r < 16; r += 2) {
+                    const int m = wm * TM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3) + (even ? 0 : 1);
+                    const int mc = min(m, cur.rows - 1);
+                    float *yrow = Yr + (int64_t)s_route[par][mc] * a.ldc;
+                    const float al = s_alpha[par][mc];
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int n = cur.n0 + wn * TN + j * 32 + 8 * g + 4 * (lane >> 5);
-                        if (n >= N) continue;
-                        *(float4 *)(yrow + n) = make_float4(al * acc[i][j][4 * g], al * acc[i][j][4 * g + 1],
-                                                            al * acc[i][j][4 * g + 2], al * acc[i][j][4 * g + 3]);
+                    for (int j = 0; j < NI; ++j) {
+                        const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+                        const float y = __int_as_float(
+                            __builtin_amdgcn_mov_dpp(__float_as_int(even ? v1 : v0), 0xB1, 0xF, 0xF, false));
+                        const float2 o = even ? make_float2(al * v0, al * y) : make_float2(al * y, al * v1);
+                        const int n = cur.n0 + wn * TN + j * 32 + cpair;
+                        if (m < cur.rows && n < N) *(float2 *)(yrow + n) = o;
                     }
                 }
             }

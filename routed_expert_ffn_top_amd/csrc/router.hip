@@ -5,8 +5,7 @@
 // Router: L[t][e] = fp32 fused multiply-add chain over the hidden index in
 // ascending order, then + bias[e]. The chain is not split or reassociated:
 // the top-k decision is taken on these bits, so they must be reproducible.
-// Each thread owns one expert column for NTOK tokens; a workgroup stages a
-// 64-wide slab of X (as fp32) and of W_r in LDS and sweeps it.
+// A lane owns one token and a few experts; W_r comes through scalar loads.
 //
 // Top-k: one wave64 per token; each lane owns experts lane, lane+64, ...
 // An expert's rank is the number of experts with a larger logit plus the
@@ -30,124 +29,245 @@ __device__ __forceinline__ float load_x<float>(const float *p) { return *p; }
 template <>
 __device__ __forceinline__ float load_x<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
 
-constexpr int kRouterKC = 64;   // hidden-index slab per LDS pass
-constexpr int kXS = kRouterKC + 4;   // padded row stride (floats) of both slabs
-
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// blockDim = 256. EPAD = E rounded up to a power of two (<= 64 here; larger
-// E uses several lanes' worth of rows); thread (g, e) owns expert e of NTOK
-// tokens g, g + groups, ... with groups = 256 / EPAD. Per 64-wide hidden slab
-// the workgroup stages X (as fp32, row per token) and W_r transposed (row per
-// expert) in LDS, double-buffered, with the next slab's global loads in
-// flight while the current one is used. Each thread reads 4 consecutive
-// hidden indices of its expert row and of each token row as 16-byte LDS
-// reads and applies the 4 fused multiply-adds in ascending order, so every
-// logit is exactly the sequential fp32 chain.
-template <typename TX, int NTOK>
+// For each expert j < NE: acc[j] += bcast(w[j], q) * x[q] for q = 0..15 in
+// ascending order, where bcast(w, q) is the value that lane q of each 16-lane
+// row holds (DPP row_newbcast:q): the 16 lanes of a row hold 16 consecutive
+// weights of one expert. The NE chains are interleaved (q outer, j inner) so
+// that consecutive multiply-adds are independent. One s_nop 1 covers the two
+// wait states a DPP source needs after a vector ALU write.
+template <int NE>
+__device__ __forceinline__ void fmac16_bcast(float *acc, const float *w, const float *x);
+
+template <>
+__device__ __forceinline__ void fmac16_bcast<1>(float *acc, const float *w, const float *x)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %10 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %11 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %12 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %13 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %14 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %15 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %1, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0])
+        : "v"(w[0]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
+}
+
+template <>
+__device__ __forceinline__ void fmac16_bcast<2>(float *acc, const float *w, const float *x)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %2, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %12 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %12 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %13 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %13 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %14 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %14 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %15 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %15 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %18 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %18 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0]), "+v"(acc[1])
+        : "v"(w[0]), "v"(w[1]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
+}
+
+template <>
+__device__ __forceinline__ void fmac16_bcast<4>(float *acc, const float *w, const float *x)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+        : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
+}
+
+// Router logits. A wave owns 64 tokens (one per lane) and NE consecutive
+// experts; the 4 waves of a workgroup take 4 expert blocks of the same 64
+// tokens (grid: T/64 x ceil(E / (4 NE))). W_r is [E][d]. The hidden index is
+// walked in 16-wide blocks: lane l loads weight (l % 16) of the block for each
+// of its experts (one coalesced 64-byte read per expert) and its own token's
+// 16 x values; a lane converts each x value once and uses it for NE chains,
+// with the weight broadcast across the row inside the multiply-add (see
+// fmac16_bcast). Loads run PF blocks ahead of the arithmetic.
+template <typename TX, int NE>
 __global__ __launch_bounds__(256) void k_router_logits(const TX *__restrict__ X, int64_t ldx,
                                                        const float *__restrict__ Wr,
                                                        const float *__restrict__ bias,
-                                                       float *__restrict__ L, int T, int d, int E,
-                                                       int epad_log2)
+                                                       float *__restrict__ L, int T, int d, int E)
 {
-    const int epad = 1 << epad_log2;
-    const int groups = 256 / epad;
-    const int tid = threadIdx.x;
-    const int e = tid & (epad - 1);
-    const int g = tid >> epad_log2;
-    const int tpw = groups * NTOK;           // tokens per workgroup
-    const int tbase = blockIdx.x * tpw;
-
-    extern __shared__ float smem[];
-    // [2][tpw][kXS] token slabs, then [2][E][kXS] transposed weight slabs
-    float *xs = smem;
-    float *ws = smem + 2 * tpw * kXS;
-
-    float acc[NTOK];
+    constexpr int PF = sizeof(TX) == 2 ? 8 : 4;
+    constexpr int XV = sizeof(TX) == 2 ? 2 : 4;   // 16-byte loads per 16 x values
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int eb = (blockIdx.y * 4 + wave) * NE;   // first expert of this wave
+    if (eb >= E) return;                           // no barriers below
+    const int t = blockIdx.x * 64 + lane;
+    const TX *xrow = X + (int64_t)min(t, T - 1) * ldx;
+    const float *wsrc[NE];
 #pragma unroll
-    for (int n = 0; n < NTOK; ++n) acc[n] = 0.0f;
+    for (int j = 0; j < NE; ++j) wsrc[j] = Wr + (int64_t)min(eb + j, E - 1) * d + (lane & 15);
 
-    const int nfull = d / kRouterKC;
-    // global -> register staging: each thread moves up to 4 X values and up
-    // to 16 W values per slab (tpw*64 <= 2048 and 64*E <= 4096 elements).
-    constexpr int XR = 8, WR = 16;
-    float xr[XR], wr[WR];
-    auto gload = [&](int c) {
-        const int i0 = c * kRouterKC;
+    float acc[NE];
 #pragma unroll
-        for (int q = 0; q < XR; ++q) {
-            const int id = q * 256 + tid;
-            const int r = id / kRouterKC, col = id % kRouterKC, t = tbase + r;
-            xr[q] = (r < tpw && t < T) ? load_x<TX>(X + (int64_t)t * ldx + i0 + col) : 0.0f;
-        }
+    for (int j = 0; j < NE; ++j) acc[j] = 0.0f;
+
+    const int nb = d >> 4;   // whole 16-wide blocks
+    auto load = [&](int b, u32x4_t *xv, float *wv) {
+        const int i0 = min(b, nb - 1) * 16;   // past the end: re-read the last block
 #pragma unroll
-        for (int q = 0; q < WR; ++q) {
-            const int id = q * 256 + tid;
-            const int r = id / E, col = id % E;
-            wr[q] = (r < kRouterKC) ? Wr[(int64_t)(i0 + r) * E + col] : 0.0f;
-        }
+        for (int h = 0; h < XV; ++h) xv[h] = *(const u32x4_t *)((const char *)(xrow + i0) + 16 * h);
+#pragma unroll
+        for (int j = 0; j < NE; ++j) wv[j] = wsrc[j][i0];
     };
-    auto sstore = [&](int buf) {
-        float *xb = xs + buf * tpw * kXS;
-        float *wb = ws + buf * E * kXS;
+    auto compute = [&](const u32x4_t *xv, const float *wv) {
+        float x[16];
+        if (sizeof(TX) == 2) {
 #pragma unroll
-        for (int q = 0; q < XR; ++q) {
-            const int id = q * 256 + tid;
-            const int r = id / kRouterKC, col = id % kRouterKC;
-            if (r < tpw) xb[r * kXS + col] = xr[q];
-        }
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t v = xv[q / 4][q % 4];
+                x[2 * q] = __uint_as_float(v << 16);
+                x[2 * q + 1] = __uint_as_float(v & 0xffff0000u);
+            }
+        } else {
 #pragma unroll
-        for (int q = 0; q < WR; ++q) {
-            const int id = q * 256 + tid;
-            const int r = id / E, col = id % E;
-            if (r < kRouterKC) wb[col * kXS + r] = wr[q];
+            for (int q = 0; q < 16; ++q) x[q] = __uint_as_float(xv[q / 4][q % 4]);
         }
+        fmac16_bcast<NE>(acc, wv, x);
     };
-
-    if (nfull > 0) {
-        gload(0);
-        sstore(0);
-    }
-    __syncthreads();
-    for (int c = 0; c < nfull; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < nfull) gload(c + 1);
-        if (e < E) {
-            const float *wrow = ws + buf * E * kXS + e * kXS;
-            const float *xb = xs + buf * tpw * kXS;
+    if (nb > 0) {
+        u32x4_t xr[PF][XV];
+        float wr[PF][NE];
 #pragma unroll
-            for (int i = 0; i < kRouterKC; i += 4) {
-                const f32x4_t w4 = *(const f32x4_t *)(wrow + i);
+        for (int u = 0; u < PF; ++u) load(u, xr[u], wr[u]);
+        int b0 = 0;
+        for (; b0 + PF <= nb; b0 += PF) {
 #pragma unroll
-                for (int n = 0; n < NTOK; ++n) {
-                    const f32x4_t x4 = *(const f32x4_t *)(xb + (g + n * groups) * kXS + i);
-                    acc[n] = __builtin_fmaf(x4.x, w4.x, acc[n]);
-                    acc[n] = __builtin_fmaf(x4.y, w4.y, acc[n]);
-                    acc[n] = __builtin_fmaf(x4.z, w4.z, acc[n]);
-                    acc[n] = __builtin_fmaf(x4.w, w4.w, acc[n]);
-                }
+            for (int u = 0; u < PF; ++u) {
+                u32x4_t xc[XV];
+                float wc[NE];
+#pragma unroll
+                for (int h = 0; h < XV; ++h) xc[h] = xr[u][h];
+#pragma unroll
+                for (int j = 0; j < NE; ++j) wc[j] = wr[u][j];
+                load(b0 + u + PF, xr[u], wr[u]);
+                compute(xc, wc);
             }
         }
-        if (c + 1 < nfull) sstore(buf ^ 1);
-        __syncthreads();
+        // the last nb - b0 < PF blocks are in the ring, block b0 + u in slot u
+#pragma unroll
+        for (int u = 0; u < PF - 1; ++u)
+            if (b0 + u < nb) compute(xr[u], wr[u]);
     }
-    // tail (d not a multiple of 64): straight from global memory, in order
-    if (e < E) {
-        for (int i = nfull * kRouterKC; i < d; ++i) {
-            const float w = Wr[(int64_t)i * E + e];
+    // hidden indices past the last whole block, in order
+    for (int i = nb * 16; i < d; ++i) {
+        const float xv = load_x<TX>(xrow + i);
 #pragma unroll
-            for (int n = 0; n < NTOK; ++n) {
-                const int t = tbase + g + n * groups;
-                if (t < T) acc[n] = __builtin_fmaf(load_x<TX>(X + (int64_t)t * ldx + i), w, acc[n]);
-            }
-        }
-        const float b = bias ? bias[e] : 0.0f;
+        for (int j = 0; j < NE; ++j)
+            acc[j] = __builtin_fmaf(xv, Wr[(int64_t)min(eb + j, E - 1) * d + i], acc[j]);
+    }
+    if (t < T) {
 #pragma unroll
-        for (int n = 0; n < NTOK; ++n) {
-            const int t = tbase + g + n * groups;
-            if (t < T) L[(int64_t)t * E + e] = bias ? acc[n] + b : acc[n];
-        }
+        for (int j = 0; j < NE; ++j)
+            if (eb + j < E) L[(int64_t)t * E + eb + j] = bias ? acc[j] + bias[eb + j] : acc[j];
     }
 }
 
@@ -243,35 +363,34 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int E
 
 }  // namespace
 
+template <typename TX, int NE>
+hipError_t launch_router_t(const moe_shape &s, const void *X, const float *Wr, const float *bias, float *L,
+                           hipStream_t st)
+{
+    const dim3 grid((s.T + 63) / 64, (s.E + 4 * NE - 1) / (4 * NE));
+    hipLaunchKernelGGL((k_router_logits<TX, NE>), grid, dim3(256), 0, st, (const TX *)X, s.ldx, Wr, bias, L,
+                       s.T, s.d, s.E);
+    return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const moe_shape &s, const void *X, const float *Wr,
                                 const float *bias, float *L, hipStream_t st)
 {
     if (s.T == 0) return hipSuccess;
-    int lg = 3;  // at least 8 expert lanes: at most 32 token groups per workgroup
-    while ((1 << lg) < s.E) ++lg;
-    if (lg > 6) return hipErrorInvalidValue;  // E <= 64 (checked by the caller)
-    const int groups = 256 >> lg;
-    const bool many = s.E >= 32;
-    const int ntok = many ? 2 : 1;
-    const int tpw = groups * ntok;            // <= 256 / EPAD * 2 <= 32 tokens
-    const dim3 grid((s.T + tpw - 1) / tpw);
-    const size_t shmem = (size_t)2 * (tpw + s.E) * kXS * sizeof(float);
+    // experts per wave: 4 while that still gives every SIMD a wave, else fewer
+    const int64_t tg = (s.T + 63) / 64;
+    int ne = tg * ((s.E + 15) / 16) >= 256 ? 4 : (tg * ((s.E + 7) / 8) >= 256 ? 2 : 1);
+#ifdef MOE_ROUTER_NE
+    ne = MOE_ROUTER_NE;
+#endif
     if (s.dtype == MOE_DT_BF16) {
-        if (many)
-            hipLaunchKernelGGL((k_router_logits<uint16_t, 2>), grid, dim3(256), shmem, st,
-                               (const uint16_t *)X, s.ldx, Wr, bias, L, s.T, s.d, s.E, lg);
-        else
-            hipLaunchKernelGGL((k_router_logits<uint16_t, 1>), grid, dim3(256), shmem, st,
-                               (const uint16_t *)X, s.ldx, Wr, bias, L, s.T, s.d, s.E, lg);
-    } else {
-        if (many)
-            hipLaunchKernelGGL((k_router_logits<float, 2>), grid, dim3(256), shmem, st,
-                               (const float *)X, s.ldx, Wr, bias, L, s.T, s.d, s.E, lg);
-        else
-            hipLaunchKernelGGL((k_router_logits<float, 1>), grid, dim3(256), shmem, st,
-                               (const float *)X, s.ldx, Wr, bias, L, s.T, s.d, s.E, lg);
+        if (ne == 4) return launch_router_t<uint16_t, 4>(s, X, Wr, bias, L, st);
+        if (ne == 2) return launch_router_t<uint16_t, 2>(s, X, Wr, bias, L, st);
+        return launch_router_t<uint16_t, 1>(s, X, Wr, bias, L, st);
     }
-    return hipGetLastError();
+    if (ne == 4) return launch_router_t<float, 4>(s, X, Wr, bias, L, st);
+    if (ne == 2) return launch_router_t<float, 2>(s, X, Wr, bias, L, st);
+    return launch_router_t<float, 1>(s, X, Wr, bias, L, st);
 }
 
 hipError_t launch_topk(const moe_shape &s, int t0, int nt, const float *L, int32_t *idx,

@@ -39,7 +39,8 @@ class MoELayer:
         self.shape = B.make_shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.n_shared, P=P,
                                   capacity=capacity, dtype=cfg.dtype, renorm=cfg.renorm)
         self.X = inp.X.to(self.device).contiguous()
-        self.Wr = inp.Wr.to(self.device).contiguous()
+        # router weight as [E][d] (one row per expert), the layout the C ABI takes
+        self.Wr = inp.Wr.to(self.device).t().contiguous()
         self.bias = None if inp.bias is None else inp.bias.to(self.device).contiguous()
         self.routes = B.alloc_routes(self.shape, self.device)
         self.ws = B.alloc_workspace(self.shape, self.device)

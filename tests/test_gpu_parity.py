@@ -12,6 +12,7 @@ import torch
 
 from gpu_util import (OracleRun, TOL, check_descriptors, check_topk, gpu_inputs, np32, rel_err,
                       sample_tokens, say)
+from oracle import oracle as oracle_mod
 from routed_expert_ffn_top_amd import binding as B
 from routed_expert_ffn_top_amd.inputs import CONFIGS, MoEConfig, make_inputs, make_logits, random_phi
 from routed_expert_ffn_top_amd.layer import MoELayer
@@ -55,10 +56,41 @@ def test_router_logits_bitexact(name):
     inp = gpu_inputs(cfg)
     s = B.make_shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.n_shared, dtype=cfg.dtype)
     L = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
-    B.moe_router_logits(s, inp.X, inp.Wr, inp.bias, L)
+    B.moe_router_logits(s, inp.X, inp.Wr.t().contiguous(), inp.bias, L)
     torch.cuda.synchronize()
     orc = OracleRun(inp)
     assert np.array_equal(L.cpu().numpy().view(np.int32), orc.L.view(np.int32))
+
+
+# (T, d, E, dtype, ldx): ragged token counts, d not a multiple of the 64-wide
+# slab (fp32 only: bf16 layers need d % 64 == 0), E not a power of two, strided X, and each tokens-per-thread choice
+ROUTER_SHAPES = [
+    (333, 320, 20, "bf16", 328),
+    (1000, 260, 60, "f32", 268),
+    (45, 64, 1, "bf16", 72),
+    (4100, 256, 64, "bf16", 256),
+    (32768, 64, 8, "bf16", 64),
+    (20000, 128, 8, "f32", 128),
+    (700, 4, 3, "f32", 4),
+    (1000, 256, 160, "bf16", 256),
+    (130, 128, 256, "bf16", 128),
+]
+
+
+@pytest.mark.parametrize("T,d,E,dtype,ldx", ROUTER_SHAPES)
+def test_router_logits_shapes(T, d, E, dtype, ldx):
+    say("router shape", T, d, E, dtype, ldx)
+    cfg = MoEConfig(name="router_shape", index=77, T=T, d=d, f=64, E=E, k=1, dtype=dtype)
+    inp = make_inputs(cfg, device="cpu")
+    Xp = torch.zeros((T, ldx), dtype=inp.X.dtype)
+    Xp[:, :d] = inp.X
+    s = B.make_shape(T, d, 64, E, 1, dtype=dtype, ldx=ldx)
+    L = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    B.moe_router_logits(s, Xp.cuda(), inp.Wr.t().contiguous().cuda(), inp.bias.cuda() if inp.bias is not None
+                        else None, L)
+    torch.cuda.synchronize()
+    ref = oracle_mod.get().router_logits(np32(inp.X), np32(inp.Wr), None if inp.bias is None else np32(inp.bias))
+    assert np.array_equal(L.cpu().numpy().view(np.int32), ref.view(np.int32))
 
 
 ROUTE_CASES = {
