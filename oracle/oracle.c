@@ -81,11 +81,14 @@ void oracle_router_logits(int64_t T, int64_t d, int64_t E, const float *X,
 
 /*
  * Top-k routing for each token t.
+ *   A NaN logit is read as -infinity (the pages define no NaN behaviour: such
+ *   an expert ranks below every number and gets weight 0).
  *   idx[t][j], j < k: the j-th choice by repeated selection of the largest
  *     logit among the experts not yet chosen; equal logits go to the lower id.
  *   alpha: p_e = exp(L_e - m) / sum_e' exp(L_e' - m) with m = max_e L_e
  *     (the softmax over all E), in fp64; alpha[t][j] = p_{idx[t][j]}, divided
- *     by sum_{j'<k} p_{idx[t][j']} when renorm != 0.
+ *     by sum_{j'<k} p_{idx[t][j']} when renorm != 0. When every logit is
+ *     -infinity, m is taken as 0 and every weight is 0.
  *   shared experts: idx[t][k + s] = E + s, alpha = 1, for s < n_shared.
  * idx and alpha are [T][k + n_shared].
  */
@@ -96,9 +99,10 @@ void oracle_topk(int64_t T, int64_t E, int64_t k, int64_t n_shared, int renorm,
     int64_t t;
 #pragma omp parallel for schedule(static)
     for (t = 0; t < T; ++t) {
-        const float *l = L + t * E;
         unsigned char *taken = (unsigned char *)calloc((size_t)E, 1);
         double *p = (double *)malloc(sizeof(double) * (size_t)E);
+        float *l = (float *)malloc(sizeof(float) * (size_t)E);
+        for (int64_t e = 0; e < E; ++e) l[e] = isnan(L[t * E + e]) ? -INFINITY : L[t * E + e];
         for (int64_t j = 0; j < k; ++j) {
             int64_t best = -1;
             for (int64_t e = 0; e < E; ++e) {
@@ -111,17 +115,18 @@ void oracle_topk(int64_t T, int64_t E, int64_t k, int64_t n_shared, int renorm,
         double m = (double)l[0];
         for (int64_t e = 1; e < E; ++e)
             if ((double)l[e] > m) m = (double)l[e];
+        if (m == -INFINITY) m = 0.0;
         double s = 0.0;
         for (int64_t e = 0; e < E; ++e) {
             p[e] = exp((double)l[e] - m);
             s += p[e];
         }
-        for (int64_t e = 0; e < E; ++e) p[e] = p[e] / s;
+        for (int64_t e = 0; e < E; ++e) p[e] = s > 0.0 ? p[e] / s : 0.0;
         double sel = 0.0;
         for (int64_t j = 0; j < k; ++j) sel += p[idx[t * kp + j]];
         for (int64_t j = 0; j < k; ++j) {
             double a = p[idx[t * kp + j]];
-            alpha[t * kp + j] = renorm ? a / sel : a;
+            alpha[t * kp + j] = renorm ? (sel > 0.0 ? a / sel : 0.0) : a;
         }
         for (int64_t s2 = 0; s2 < n_shared; ++s2) {
             idx[t * kp + k + s2] = (int32_t)(E + s2);
@@ -129,6 +134,7 @@ void oracle_topk(int64_t T, int64_t E, int64_t k, int64_t n_shared, int renorm,
         }
         free(taken);
         free(p);
+        free(l);
     }
 }
 

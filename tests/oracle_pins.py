@@ -169,6 +169,28 @@ def check_topk_special(orc):
     assert abs(al[0, 3] - math.exp(2) / z) < 1e-15
 
 
+def check_topk_nan_and_signed_zero(orc):
+    """Reading of the routing step for values the pages leave open: a NaN
+    logit ranks as -infinity with weight 0; -0 and +0 are equal logits (tie
+    to the lower id); a row with no finite logit picks ids in order with
+    weight 0."""
+    nan, inf = float("nan"), float("inf")
+    h = np.array([[nan, 1.0, 0.5, nan, -0.0, 0.0],
+                  [nan, nan, nan, nan, nan, nan],
+                  [0.0, -0.0, nan, -inf, -0.0, 0.0]], dtype=np.float32)
+    idx, al = orc.topk(h, 3, 0, True)
+    assert idx.tolist()[0] == [1, 2, 4]                 # -0 at id 4 before +0 at id 5
+    z = math.exp(1.0) + math.exp(0.5) + 2 * math.exp(0.0)
+    p = [math.exp(1.0) / z, math.exp(0.5) / z, 1.0 / z]
+    assert max(abs(al[0, j] - p[j] / sum(p)) for j in range(3)) < 1e-15
+    assert idx.tolist()[1] == [0, 1, 2] and np.all(al[1] == 0.0)
+    assert idx.tolist()[2] == [0, 1, 4]                 # four equal zeros: the lowest ids
+    assert max(abs(al[2, j] - 1.0 / 3.0) for j in range(3)) < 1e-15
+    idx, al = orc.topk(h, 3, 0, False)
+    assert max(abs(al[0, j] - p[j]) for j in range(3)) < 1e-15
+    assert max(abs(al[2, j] - 0.25) for j in range(3)) < 1e-15   # 4 zeros share the mass
+
+
 def check_alpha(orc):
     rng = _rng(23)
     T, E = 40, 64
@@ -365,6 +387,7 @@ def check_layer_chain(orc):
 
 
 ALL_CHECKS = [check_router_golden, check_router_exact_integers, check_router_error_bound,
-              check_topk_bruteforce, check_topk_special, check_alpha, check_shared,
+              check_topk_bruteforce, check_topk_special, check_topk_nan_and_signed_zero, check_alpha,
+              check_shared,
               check_route_map_golden, check_route_map_bruteforce, check_route_map_errors,
               check_ffn_dense_bruteforce, check_ffn_special, check_layer_chain]

@@ -22,7 +22,8 @@ MUTANTS = [
     ("router rounds each product", "acc = fmaf(X[t * ldx + i], Wr[i * E + e], acc);",
      "acc = acc + X[t * ldx + i] * Wr[i * E + e];"),
     ("top-k ties go to the higher id", "l[e] > l[best]", "l[e] >= l[best]"),
-    ("renormalisation inverted", "renorm ? a / sel : a", "renorm ? a : a / sel"),
+    ("renormalisation inverted", "renorm ? (sel > 0.0 ? a / sel : 0.0) : a", "renorm ? a : (sel > 0.0 ? a / sel : 0.0)"),
+    ("NaN logits not read as -infinity", "isnan(L[t * E + e]) ? -INFINITY : L[t * E + e]", "L[t * E + e]"),
     ("softmax denominator skips the last expert",
      "for (int64_t e = 0; e < E; ++e) {\n            p[e] = exp",
      "for (int64_t e = 0; e < E; ++e) {\n            if (e == E - 1) { p[e] = 0.0; continue; }\n            p[e] = exp"),
