@@ -265,7 +265,7 @@ def main() -> int:
     ms = start.elapsed_time(stop) / K
 
     # per-kernel breakdown: a second pass with every kernel bracketed
-    names = ["router", "topk", "route_count", "route_scan", "route_place", "gate_up", "down", "combine"]
+    names = ["router", "topk", "route_count", "route_place", "gate_up", "down", "combine"]
     reps = min(K, 10)
     for nme in names:
         B.moe_profile_begin(nme, reps)

@@ -331,12 +331,11 @@ moe_status moe_selftest_mfma_layout(float *out, moe_stream stream);
 #define MOE_KERNEL_ROUTER 1
 #define MOE_KERNEL_TOPK 2
 #define MOE_KERNEL_ROUTE_COUNT 3
-#define MOE_KERNEL_ROUTE_SCAN 4
-#define MOE_KERNEL_ROUTE_PLACE 5
-#define MOE_KERNEL_GATE_UP 6
-#define MOE_KERNEL_DOWN 7
-#define MOE_KERNEL_COMBINE 8
-#define MOE_KERNEL_COUNT 9
+#define MOE_KERNEL_ROUTE_PLACE 4
+#define MOE_KERNEL_GATE_UP 5
+#define MOE_KERNEL_DOWN 6
+#define MOE_KERNEL_COMBINE 7
+#define MOE_KERNEL_COUNT 8
 /* moe_profile_begin arms timing of one kernel id for the next max_launches
  * launches (process-wide): each such launch is bracketed by a pair of HIP
  * events recorded on the launch's stream. moe_profile_end waits for those

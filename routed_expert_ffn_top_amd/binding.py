@@ -81,8 +81,8 @@ _SIGS = {
     "moe_profile_end": ([_I32, _VP, _I32, _VP], _I32),
 }
 
-MOE_KERNEL = {"router": 1, "topk": 2, "route_count": 3, "route_scan": 4, "route_place": 5,
-              "gate_up": 6, "down": 7, "combine": 8}
+MOE_KERNEL = {"router": 1, "topk": 2, "route_count": 3, "route_place": 4, "gate_up": 5, "down": 6,
+              "combine": 7}
 
 
 def lib_path() -> str:

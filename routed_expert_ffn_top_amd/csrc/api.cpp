@@ -323,18 +323,15 @@ moe_status route_build_impl(const moe_shape &s, const WsLayout &w, int t0, int n
         reset = 0;  // top-k cleared the marks of the range
     }
     const int64_t i0 = (int64_t)t0 * kp, n = (int64_t)nt * kp;
-    const int nblk = (int)((n + kRouteBlock - 1) / kRouteBlock);
     int32_t *blk = ws_at<int32_t>(ws, w.blk);
     int32_t *rank = ws_at<int32_t>(ws, w.rank);
     int32_t *err = ws_at<int32_t>(ws, w.err);
     HIP_TRY(TIMED(MOE_KERNEL_ROUTE_COUNT, st,
                   launch_route_count(s, i0, n, r.topk_idx, phi, blk, rank, err, done, reset, st)),
             "route count launch");
-    HIP_TRY(TIMED(MOE_KERNEL_ROUTE_SCAN, st, launch_route_scan(s, nblk, blk, r.slot_count, r.slot_offset, st)),
-            "route scan launch");
     HIP_TRY(TIMED(MOE_KERNEL_ROUTE_PLACE, st,
                   launch_route_place(s, i0, n, r.topk_idx, phi, blk, rank, r.rec_token, r.rec_route,
-                                     r.route_pos, st)),
+                                     r.route_pos, r.slot_count, r.slot_offset, st)),
             "route place launch");
     return MOE_OK;
 }

@@ -80,12 +80,10 @@ hipError_t launch_topk(const moe_shape &s, int t0, int nt, const float *L, int32
 hipError_t launch_route_count(const moe_shape &s, int64_t i0, int64_t n, const int32_t *idx,
                               const PhiArg &phi, int32_t *blk, int32_t *rank, int32_t *err,
                               int32_t *done, int reset, hipStream_t st);
-hipError_t launch_route_scan(const moe_shape &s, int nblk, int32_t *blk, int32_t *count,
-                             int32_t *offset, hipStream_t st);
 hipError_t launch_route_place(const moe_shape &s, int64_t i0, int64_t n, const int32_t *idx,
                               const PhiArg &phi, const int32_t *blk, const int32_t *rank,
                               int32_t *rec_token, int32_t *rec_route, int32_t *route_pos,
-                              hipStream_t st);
+                              int32_t *count, int32_t *offset, hipStream_t st);
 hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
                           hipStream_t st);
 hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,

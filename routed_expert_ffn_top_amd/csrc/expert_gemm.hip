@@ -411,14 +411,20 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     const char *asrc[AI];
     const char *bsrc[BI];
     const int lr = lane >> 2, lp = lane & 3;
-    auto set_sources = [&](const TileInfo &t) {
+    // A row of each of this lane's copies (gathered token rows for gate/up)
+    auto fetch_rows = [&](const TileInfo &t, int32_t *rows) {
+#pragma unroll
+        for (int j = 0; j < AI; ++j) {
+            const int rr = min((wave * AI + j) * 16 + lr, t.rows - 1);
+            rows[j] = GATEUP ? a.rec_token[t.row0 + rr] : t.row0 + rr;
+        }
+    };
+    auto set_sources = [&](const TileInfo &t, const int32_t *rows) {
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
             const int r = (wave * AI + j) * 16 + lr;
             const int c = lp ^ ((r >> 2) & 3);
-            const int rr = min(r, t.rows - 1);
-            const int64_t arow = GATEUP ? (int64_t)a.rec_token[t.row0 + rr] : (int64_t)(t.row0 + rr);
-            asrc[j] = (const char *)a.A + (arow * a.lda) * 2 + c * 16;
+            asrc[j] = (const char *)a.A + ((int64_t)rows[j] * a.lda) * 2 + c * 16;
         }
         const char *Bslot = (const char *)a.B + (int64_t)t.slot * a.slot_stride * 2;
 #pragma unroll
@@ -429,13 +435,21 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
             bsrc[j] = Bslot + (int64_t)n * K * 2 + c * 16;
         }
     };
-    auto load_routes = [&](const TileInfo &t, int par) {
-        if (!GATEUP) {
-            for (int m = tid; m < BM; m += NT) {
-                const int rt = a.rec_route[t.row0 + min(m, t.rows - 1)];
-                s_route[par][m] = rt;
-                s_alpha[par][m] = a.topk_w[rt];
-            }
+    // down: route id and alpha of tile row tid (threads tid < BM), staged in
+    // registers and then stored to the LDS copy of the given parity
+    static_assert(NT >= BM, "one route per thread");
+    int32_t pre_rt = 0;
+    float pre_al = 0.0f;
+    auto fetch_route = [&](const TileInfo &t) {
+        if (!GATEUP && tid < BM) pre_rt = a.rec_route[t.row0 + min(tid, t.rows - 1)];
+    };
+    auto fetch_alpha = [&]() {
+        if (!GATEUP && tid < BM) pre_al = a.topk_w[pre_rt];
+    };
+    auto store_routes = [&](int par) {
+        if (!GATEUP && tid < BM) {
+            s_route[par][tid] = pre_rt;
+            s_alpha[par][tid] = pre_al;
         }
     };
     auto issue = [&](int kt) {
@@ -488,14 +502,25 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     const int nk = K / BK;
     int tl = li, par = 0;
     TileInfo cur = decode(start_x + tl);
-    set_sources(cur);
-    load_routes(cur, 0);
+    int32_t rows[AI];
+    fetch_rows(cur, rows);
+    set_sources(cur, rows);
+    fetch_route(cur);
+    fetch_alpha();
+    store_routes(0);
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p)
         if (p < nk) issue(p);
 
     for (;;) {
         const bool wave_active = wm * TM < cur.rows;
+        // The next tile of this workgroup (nwg further on in the XCD's range):
+        // its row indices, route ids and alphas are requested during the first
+        // two steps of this tile, so that the switch at the end of the tile
+        // waits on nothing.
+        const int tn = tl + nwg;
+        const bool has_next = tn < cnt_x;
+        const TileInfo nxt = has_next ? decode(start_x + tn) : cur;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -534,8 +559,13 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                 // last read by fragment loads whose results fed MFMAs issued
                 // before this point, so no LDS counter needs draining here.
                 __builtin_amdgcn_s_barrier();
-                if (kt + NS - 1 < nk) issue(kt + NS - 1);
             }
+            if (has_next && kt == 0) {
+                fetch_rows(nxt, rows);
+                fetch_route(nxt);
+            }
+            if (has_next && kt == 1) fetch_alpha();
+            if (more && kt + NS - 1 < nk) issue(kt + NS - 1);
             if (wave_active) {
                 read_frags(stage, 1, 1);
                 mfmas(0);
@@ -551,17 +581,14 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         // Start the next tile's copies before this tile's epilogue, which
         // works from registers: once every wave is past this barrier nothing
         // reads the ring any more.
-        const int tn = tl + nwg;
-        const bool has_next = tn < cnt_x;
-        TileInfo nxt = cur;
         if (has_next) {
-            nxt = decode(start_x + tn);
+            if (nk < 2) fetch_alpha();
             __syncthreads();
-            set_sources(nxt);
+            set_sources(nxt, rows);
 #pragma unroll
             for (int p = 0; p < NS - 1; ++p)
                 if (p < nk) issue(p);
-            load_routes(nxt, par ^ 1);  // the other parity: last read two tiles ago
+            store_routes(par ^ 1);  // the other parity: last read two tiles ago
         }
 
         // Result layout: register r of lane l holds row 8*(r/4) + 4*(l/32) +

@@ -10,10 +10,11 @@
 //            slot key (popcount of the same-key lanes below it), across the
 //            block's 4 waves from per-wave counts in LDS. The block's
 //            per-slot counts go to blk[b][s].
-//   scan   - one workgroup turns blk into absolute bases:
-//            base[b][s] = offset[s] + sum_{b' < b} blk[b'][s],
-//            and writes count[s], offset[s] (exclusive), offset[P].
-//   place  - p = base[b][psi_i] + rank_i gives exactly the position the
+//   place  - each block first forms its absolute bases from the whole blk
+//            matrix: base[b][s] = offset[s] + sum_{b' < b} blk[b'][s], with
+//            offset the exclusive prefix over slots of the column sums (block
+//            0 also writes count[s], offset[s] and offset[P]); then
+//            p = base[b][psi_i] + rank_i gives exactly the position the
 //            sequential cursor pass would give, since both order records of a
 //            slot by ascending route id.
 // All arithmetic is integer, so the descriptors are bit-exact and
@@ -90,62 +91,66 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane)
     return v;
 }
 
-// One workgroup of 1024 threads (16 waves).
-__global__ __launch_bounds__(1024) void k_route_scan(int32_t *__restrict__ blk, int nblk, int P,
-                                                     int32_t *__restrict__ count,
-                                                     int32_t *__restrict__ offset)
-{
-    __shared__ int32_t tot[kMaxExp];
-    __shared__ int32_t off[kMaxExp + 1];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    // per slot: exclusive scan over blocks
-    for (int s = wave; s < P; s += 16) {
-        int run = 0;
-        for (int b0 = 0; b0 < nblk; b0 += 64) {
-            const int b = b0 + lane;
-            const int v = b < nblk ? blk[(int64_t)b * P + s] : 0;
-            const int inc = wave_incl_scan(v, lane);
-            if (b < nblk) blk[(int64_t)b * P + s] = run + inc - v;
-            run += __shfl(inc, 63, 64);
-        }
-        if (lane == 0) tot[s] = run;
-    }
-    __syncthreads();
-    if (wave == 0) {
-        int run = 0;
-        for (int s0 = 0; s0 < P; s0 += 64) {
-            const int s = s0 + lane;
-            const int v = s < P ? tot[s] : 0;
-            const int inc = wave_incl_scan(v, lane);
-            if (s < P) {
-                off[s] = run + inc - v;
-                count[s] = v;
-                offset[s] = run + inc - v;
-            }
-            run += __shfl(inc, 63, 64);
-        }
-        if (lane == 0) {
-            off[P] = run;
-            offset[P] = run;
-        }
-    }
-    __syncthreads();
-    for (int64_t q = tid; q < (int64_t)nblk * P; q += 1024) blk[q] += off[q % P];
-}
-
+// blockDim = 256 = kRouteBlock. blk holds the per-block slot counts of the
+// count pass (nblk x P, unscanned).
 __global__ __launch_bounds__(256) void k_route_place(const int32_t *__restrict__ idx, int64_t i0,
-                                                     int64_t n, int kp, int n_exp, int P,
+                                                     int64_t n, int kp, int n_exp, int P, int nblk,
                                                      PhiArg phi, const int32_t *__restrict__ blk,
                                                      const int32_t *__restrict__ rank,
                                                      int32_t *__restrict__ rec_token,
                                                      int32_t *__restrict__ rec_route,
-                                                     int32_t *__restrict__ route_pos)
+                                                     int32_t *__restrict__ route_pos,
+                                                     int32_t *__restrict__ count,
+                                                     int32_t *__restrict__ offset)
 {
     __shared__ int32_t sphi[kMaxExp];
-    const int tid = threadIdx.x;
+    __shared__ int32_t part_before[4][64], part_tot[4][64];
+    __shared__ int32_t sbase[kMaxExp], stot[kMaxExp];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int b = blockIdx.x;
     for (int q = tid; q < n_exp; q += 256) sphi[q] = phi.v[q];
+    // column sums of blk: all blocks (total) and blocks before this one;
+    // 64 slots at a time, each wave summing every 4th block
+    for (int s0 = 0; s0 < P; s0 += 64) {
+        const int s = s0 + lane;
+        int before = 0, tot = 0;
+        if (s < P) {
+#pragma unroll 8
+            for (int b2 = wave; b2 < nblk; b2 += 4) {
+                const int v = blk[(int64_t)b2 * P + s];
+                tot += v;
+                before += b2 < b ? v : 0;
+            }
+        }
+        part_before[wave][lane] = before;
+        part_tot[wave][lane] = tot;
+        __syncthreads();
+        if (wave == 0 && s < P) {
+            sbase[s] = part_before[0][lane] + part_before[1][lane] + part_before[2][lane] + part_before[3][lane];
+            stot[s] = part_tot[0][lane] + part_tot[1][lane] + part_tot[2][lane] + part_tot[3][lane];
+        }
+        __syncthreads();
+    }
+    // exclusive prefix over slots, added to the bases
+    if (wave == 0) {
+        int run = 0;
+        for (int s0 = 0; s0 < P; s0 += 64) {
+            const int s = s0 + lane;
+            const int v = s < P ? stot[s] : 0;
+            const int inc = wave_incl_scan(v, lane);
+            if (s < P) {
+                sbase[s] += run + inc - v;
+                if (b == 0) {
+                    count[s] = v;
+                    offset[s] = run + inc - v;
+                }
+            }
+            run += __shfl(inc, 63, 64);
+        }
+        if (b == 0 && lane == 0) offset[P] = run;
+    }
     __syncthreads();
-    const int64_t r = (int64_t)blockIdx.x * kRouteBlock + tid;
+    const int64_t r = (int64_t)b * kRouteBlock + tid;
     if (r >= n) return;
     const int64_t i = i0 + r;
     const int e = idx[i];
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(256) void k_route_place(const int32_t *__restrict__
         route_pos[i] = -1;
         return;
     }
-    const int p = blk[(int64_t)blockIdx.x * P + psi] + rank[r];
+    const int p = sbase[psi] + rank[r];
     rec_token[p] = (int32_t)(i / kp);
     rec_route[p] = (int32_t)i;
     route_pos[i] = p;
@@ -195,23 +200,16 @@ hipError_t launch_route_count(const moe_shape &s, int64_t i0, int64_t n, const i
     return hipGetLastError();
 }
 
-hipError_t launch_route_scan(const moe_shape &s, int nblk, int32_t *blk, int32_t *count,
-                             int32_t *offset, hipStream_t st)
-{
-    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, blk, nblk, s.P, count, offset);
-    return hipGetLastError();
-}
-
 hipError_t launch_route_place(const moe_shape &s, int64_t i0, int64_t n, const int32_t *idx,
                               const PhiArg &phi, const int32_t *blk, const int32_t *rank,
                               int32_t *rec_token, int32_t *rec_route, int32_t *route_pos,
-                              hipStream_t st)
+                              int32_t *count, int32_t *offset, hipStream_t st)
 {
-    if (n == 0) return hipSuccess;
-    const dim3 grid((unsigned)((n + kRouteBlock - 1) / kRouteBlock));
-    hipLaunchKernelGGL(k_route_place, grid, dim3(kRouteBlock), 0, st, idx, i0, n,
-                       s.k + s.n_shared, s.E + s.n_shared, s.P, phi, blk, rank, rec_token,
-                       rec_route, route_pos);
+    // at least one block: block 0 writes count and offset even for n == 0
+    const int nblk = (int)((n + kRouteBlock - 1) / kRouteBlock);
+    hipLaunchKernelGGL(k_route_place, dim3(nblk > 0 ? nblk : 1), dim3(kRouteBlock), 0, st, idx, i0, n,
+                       s.k + s.n_shared, s.E + s.n_shared, s.P, nblk, phi, blk, rank, rec_token, rec_route,
+                       route_pos, count, offset);
     return hipGetLastError();
 }
 

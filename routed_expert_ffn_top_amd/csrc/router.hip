@@ -285,16 +285,30 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-constexpr int kTopkMaxPerLane = 4;   // E <= 256
+// Order-preserving 64-bit key of (logit, expert): a larger key means a larger
+// logit, or an equal logit and a lower expert id. NaN is taken as -infinity
+// and -0 as +0, so equal logits give equal high words.
+__device__ __forceinline__ uint64_t topk_key(float x, int e)
+{
+    if (x != x) x = -__builtin_huge_valf();
+    if (x == 0.0f) x = 0.0f;
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+}
 
-// blockDim = 256: 4 waves, one token each. Writes ranks 0..k-1 (routed) and
-// k..K'-1 (shared) of idx/w for the tokens in [t0, t0 + nt).
+// Top-k for one token per wave; lane l holds experts l, l+64, ... (C per
+// lane, C = ceil(E/64)). An expert's rank is the number of experts with a
+// larger key: ranks are unique, ties go to the lower id, and the experts of
+// rank < k are the selection in rank order. Softmax max and sums use fixed
+// xor-butterfly reductions.
+template <int C>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int E, int k,
                                               int n_shared, int renorm, int t0, int nt,
                                               int32_t *__restrict__ idx, float *__restrict__ w,
                                               int32_t *__restrict__ done)
 {
-    __shared__ float vals[4][256];
+    __shared__ uint64_t keys[4][64 * C + 2];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int tl = blockIdx.x * 4 + wave;
     const bool active = tl < nt;
@@ -302,42 +316,43 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int E
     const int kp = k + n_shared;
     const float NEG_INF = -__builtin_huge_valf();
 
-    float v[kTopkMaxPerLane];
+    float v[C];
+    uint64_t key[C];
 #pragma unroll
-    for (int c = 0; c < kTopkMaxPerLane; ++c) {
+    for (int c = 0; c < C; ++c) {
         const int e = lane + 64 * c;
         float x = NEG_INF;
         if (e < E) {
             x = L[(int64_t)t * E + e];
-            if (x != x) x = NEG_INF;  // NaN counts as -infinity
-            vals[wave][e] = x;
+            if (x != x) x = NEG_INF;
         }
         v[c] = x;
+        key[c] = topk_key(x, e);
+        keys[wave][e] = e < E ? key[c] : 0ull;   // padding keys rank below every expert
     }
+    if (lane < 2) keys[wave][64 * C + lane] = 0ull;
     __syncthreads();
     if (!active) return;
 
-    int rank[kTopkMaxPerLane];
+    int rank[C];
 #pragma unroll
-    for (int c = 0; c < kTopkMaxPerLane; ++c) rank[c] = 0;
-    for (int e2 = 0; e2 < E; ++e2) {
-        const float x2 = vals[wave][e2];
+    for (int c = 0; c < C; ++c) rank[c] = 0;
+    const int E2 = (E + 1) & ~1;
+    for (int e2 = 0; e2 < E2; e2 += 2) {
+        const uint64_t k0 = keys[wave][e2], k1 = keys[wave][e2 + 1];
 #pragma unroll
-        for (int c = 0; c < kTopkMaxPerLane; ++c) {
-            const int e = lane + 64 * c;
-            rank[c] += (x2 > v[c]) || (x2 == v[c] && e2 < e);
-        }
+        for (int c = 0; c < C; ++c) rank[c] += (int)(k0 > key[c]) + (int)(k1 > key[c]);
     }
 
     float m = NEG_INF;
 #pragma unroll
-    for (int c = 0; c < kTopkMaxPerLane; ++c) m = fmaxf(m, v[c]);
+    for (int c = 0; c < C; ++c) m = fmaxf(m, v[c]);
     m = wave_max(m);
     if (m == NEG_INF) m = 0.0f;
-    float z[kTopkMaxPerLane];
+    float z[C];
     float s = 0.0f, ssel = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kTopkMaxPerLane; ++c) {
+    for (int c = 0; c < C; ++c) {
         const int e = lane + 64 * c;
         z[c] = (e < E) ? expf(v[c] - m) : 0.0f;
         s += z[c];
@@ -347,7 +362,7 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int E
     ssel = wave_sum(ssel);
     const float den = renorm ? ssel : s;
 #pragma unroll
-    for (int c = 0; c < kTopkMaxPerLane; ++c) {
+    for (int c = 0; c < C; ++c) {
         const int e = lane + 64 * c;
         if (e < E && rank[c] < k) {
             idx[(int64_t)t * kp + rank[c]] = e;
@@ -398,8 +413,15 @@ hipError_t launch_topk(const moe_shape &s, int t0, int nt, const float *L, int32
 {
     if (nt == 0) return hipSuccess;
     const dim3 grid((nt + 3) / 4);
-    hipLaunchKernelGGL(k_topk, grid, dim3(256), 0, st, L, s.E, s.k, s.n_shared, s.renorm, t0,
-                       nt, idx, w, done);
+    if (s.E <= 64)
+        hipLaunchKernelGGL(k_topk<1>, grid, dim3(256), 0, st, L, s.E, s.k, s.n_shared, s.renorm, t0, nt, idx, w,
+                           done);
+    else if (s.E <= 128)
+        hipLaunchKernelGGL(k_topk<2>, grid, dim3(256), 0, st, L, s.E, s.k, s.n_shared, s.renorm, t0, nt, idx, w,
+                           done);
+    else
+        hipLaunchKernelGGL(k_topk<4>, grid, dim3(256), 0, st, L, s.E, s.k, s.n_shared, s.renorm, t0, nt, idx, w,
+                           done);
     return hipGetLastError();
 }
 

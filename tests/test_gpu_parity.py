@@ -105,6 +105,9 @@ ROUTE_CASES = {
     "wide_P": (513, 20, 3, 1, True, 100, 0, 0, 513, "normal"),
     "range": (600, 64, 8, 0, True, 64, 0, 123, 200, "normal"),
     "one_token": (1, 64, 8, 0, True, 64, 0, 0, 1, "normal"),
+    "many_blocks": (9000, 64, 8, 0, True, 64, 0, 0, 9000, "normal"),
+    "zeros_nan": (300, 40, 5, 0, True, 40, 0, 0, 300, "zeros_nan"),
+    "wide_E": (200, 200, 6, 0, False, 200, 0, 0, 200, "ties"),
     "skewed": (2048, 64, 8, 0, True, 64, 0, 0, 2048, "skewed"),
 }
 
@@ -116,6 +119,11 @@ def test_route_build_bitexact(case):
     L = make_logits(T, E, seed=100 + len(case))
     if kind == "ties":
         L = torch.round(L * 2) / 2      # many exactly equal logits
+    if kind == "zeros_nan":
+        L = torch.round(L)              # many ties, many exact zeros
+        L[L == 0] = torch.where(torch.rand(int((L == 0).sum()), generator=torch.Generator().manual_seed(5)) < 0.5,
+                                torch.tensor(-0.0), torch.tensor(0.0))
+        L[::7, 3] = float("nan")        # NaN ranks as -infinity
     if kind == "skewed":
         L[:, 5] += 6.0                  # nearly every token picks expert 5
         L[:, 9] -= 30.0                 # expert 9 is never picked
