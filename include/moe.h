@@ -335,7 +335,8 @@ moe_status moe_selftest_mfma_layout(float *out, moe_stream stream);
 #define MOE_KERNEL_GATE_UP 5
 #define MOE_KERNEL_DOWN 6
 #define MOE_KERNEL_COMBINE 7
-#define MOE_KERNEL_COUNT 8
+#define MOE_KERNEL_H2D 8        /* the two host-to-device copies of one bind */
+#define MOE_KERNEL_COUNT 9
 /* moe_profile_begin arms timing of one kernel id for the next max_launches
  * launches (process-wide): each such launch is bracketed by a pair of HIP
  * events recorded on the launch's stream. moe_profile_end waits for those

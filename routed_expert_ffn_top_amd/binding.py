@@ -82,7 +82,7 @@ _SIGS = {
 }
 
 MOE_KERNEL = {"router": 1, "topk": 2, "route_count": 3, "route_place": 4, "gate_up": 5, "down": 6,
-              "combine": 7}
+              "combine": 7, "h2d": 8}
 
 
 def lib_path() -> str:

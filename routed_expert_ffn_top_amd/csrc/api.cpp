@@ -251,11 +251,14 @@ moe_status arena_bind_locked(moe_arena *a, int slot, int expert, const void *src
     hipError_t e = hipSuccess;
     if (rc == MOE_OK && a->last_use[slot] >= 0) e = hipStreamWaitEvent(st, a->ring[a->last_use[slot]], 0);
     if (rc == MOE_OK && e == hipSuccess)
-        e = hipMemcpyAsync(a->plane_gu + (size_t)slot * a->stride_gu * a->esz, src_gu, gu_bytes,
-                           hipMemcpyDefault, st);
-    if (rc == MOE_OK && e == hipSuccess)
-        e = hipMemcpyAsync(a->plane_d + (size_t)slot * a->stride_d * a->esz, src_d, d_bytes,
-                           hipMemcpyDefault, st);
+        e = TIMED(MOE_KERNEL_H2D, st, [&]() {
+            hipError_t r = hipMemcpyAsync(a->plane_gu + (size_t)slot * a->stride_gu * a->esz, src_gu, gu_bytes,
+                                          hipMemcpyDefault, st);
+            if (r == hipSuccess)
+                r = hipMemcpyAsync(a->plane_d + (size_t)slot * a->stride_d * a->esz, src_d, d_bytes,
+                                   hipMemcpyDefault, st);
+            return r;
+        }());
     if (rc == MOE_OK && e == hipSuccess) e = hipEventRecord(a->ready[slot], st);
     if (rc != MOE_OK || e != hipSuccess) {
         arena_abort_fill(a, slot);
@@ -723,7 +726,8 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
     HIP_TRY(TIMED(MOE_KERNEL_TOPK, cs,
                   launch_topk(s, 0, s.T, L, routes->topk_idx, routes->topk_w, ws_at<int32_t>(ws, w.done), cs)),
             "top-k launch");
-    HIP_TRY(launch_expert_hist(s, routes->topk_idx, (int64_t)s.T * kp, ws_at<int32_t>(ws, w.ecount), cs),
+    HIP_TRY(TIMED(MOE_KERNEL_ROUTE_COUNT, cs,
+                  launch_expert_hist(s, routes->topk_idx, (int64_t)s.T * kp, ws_at<int32_t>(ws, w.ecount), cs)),
             "histogram launch");
     std::vector<int32_t> ecount(ne, 0);
     HIP_TRY(hipMemcpyAsync(ecount.data(), ws_at<int32_t>(ws, w.ecount), ne * 4, hipMemcpyDeviceToHost, cs),
