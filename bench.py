@@ -49,6 +49,10 @@ for _t in (256, 512, 1024, 2048, 4096):
     WORKLOAD_TEXT[f"virt_olmoe_t{_t}"] = (
         f"OLMoE-shaped MoE layer with experts paged from pinned host memory: T={_t}, d=2048, E=64, "
         "top-8 with a Zipf(1.1) popularity bias, f=1024, bf16; P=16 arena slots in 2 banks of G=8")
+for _t in (256, 1024, 4096):
+    WORKLOAD_TEXT[f"mixtral_stack_t{_t}"] = (
+        f"32 Mixtral-8x7B-shaped MoE layers with independent weights, all resident (90.2 GB): T={_t}, "
+        "d=4096, E=8, top-2 renormalised, SwiGLU f=14336, bf16; only the MoE sublayers are timed")
 PCIE_GEN5_X16_GBS = 64.0   # one direction, before protocol overhead
 
 
@@ -289,6 +293,63 @@ def bench_paged(args, cfg) -> int:
     return 0
 
 
+def bench_stack(args, cfg, n_layers: int = 32) -> int:
+    """A stack of n_layers MoE layers with independent weights (each layer's
+    own seeded X, router and experts), all resident in HBM; one step runs the
+    layers back to back on one stream. Reports the stack time and the
+    per-layer average."""
+    import torch
+
+    from routed_expert_ffn_top_amd.inputs import make_inputs
+    from routed_expert_ffn_top_amd.layer import MoELayer
+
+    layers, outs = [], []
+    for l in range(n_layers):
+        inp = make_inputs(cfg, layer=l, device="cuda", residual=False)
+        layers.append(MoELayer(inp))
+        outs.append(torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda"))
+        del inp
+        torch.cuda.empty_cache()
+        print(f"built layer {l + 1}/{n_layers}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for lay, Y in zip(layers, outs):
+            lay.forward(Y)
+    torch.cuda.synchronize()
+    K = args.steps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(K):
+        for lay, Y in zip(layers, outs):
+            lay.forward(Y)
+    b.record()
+    torch.cuda.synchronize()
+    stack_ms = a.elapsed_time(b) / K
+    R = cfg.T * cfg.kp
+    flops = 6.0 * R * cfg.d * cfg.f * n_layers
+    out = {
+        "metric": f"routed tokens/s through {n_layers} MoE layers (1 GPU)",
+        "value": round(cfg.T / (stack_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(stack_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights per layer)",
+        "config": {"workload": WORKLOAD_TEXT[f"mixtral_stack_t{cfg.T}"], "T": cfg.T, "d": cfg.d, "E": cfg.E,
+                   "k": cfg.k, "f": cfg.f, "layers": n_layers},
+        "per_layer_ms": round(stack_ms / n_layers, 4),
+        "stack_ms": round(stack_ms, 3),
+        "pct_bf16_peak": round(100.0 * flops / (stack_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "resident_expert_gb": round(n_layers * cfg.n_exp * 3 * cfg.d * cfg.f * 2 / 1e9, 1),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,9 +397,11 @@ def main() -> int:
         return 0
 
     B.load()
-    cfg = CONFIGS[args.workload]
     if args.workload.startswith("virt_"):
-        return bench_paged(args, cfg)
+        return bench_paged(args, CONFIGS[args.workload])
+    if args.workload.startswith("mixtral_stack_"):
+        return bench_stack(args, CONFIGS[args.workload.replace("mixtral_stack_", "mixtral_")])
+    cfg = CONFIGS[args.workload]
     inp = make_inputs(cfg, device="cuda", residual=False)
     layer = MoELayer(inp)
     Y = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
