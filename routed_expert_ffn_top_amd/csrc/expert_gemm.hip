@@ -134,178 +134,12 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u)
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel. WM x WN waves; each wave computes a (BM/WM) x (BN/WN)
-// block as 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16), K step 64,
-// double-buffered LDS with a 16-byte pad per row (conflict-free 16-byte
-// fragment reads: 8 lanes reading 8 rows touch all 32 banks once).
-// MFMA operand layout (32x32x16): lane l supplies row (l % 32) and the 8
-// consecutive k values 8*(l / 32) .. +7 of A (and of B^T); result register r
-// of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
-template <int BM, int BN, int WM, int WN, bool GATEUP>
-__global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma(GemmArgs a)
-{
-    constexpr int NT = WM * WN * 64;
-    constexpr int BK = 64, LDK = BK + 8;
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int MI = TM / 32, NI = TN / 32;
-    constexpr int CA = BM * BK / 8 / NT, CB = BN * BK / 8 / NT;
-    static_assert(CA >= 1 && CB >= 1 && MI >= 1 && NI >= 1, "tile shape");
-    static_assert(!GATEUP || (TN % 64) == 0, "gate/up pairs need 64-column wave tiles");
-
-    __shared__ TileInfo ti;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * LDK];
-    __shared__ int32_t s_route[GATEUP ? 1 : BM];
-    __shared__ float s_alpha[GATEUP ? 1 : BM];
-
-    if (!find_tile<BM, BN>(a, &ti)) return;
-    const int slot = ti.slot, row0 = ti.row0, rows = ti.rows, n0 = ti.n0;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = __builtin_amdgcn_readfirstlane(wave / WN), wn = __builtin_amdgcn_readfirstlane(wave % WN);
-    const int K = a.K, N = a.N;
-    // a wave whose rows all lie past the tile's valid rows does no MFMA work
-    const bool wave_active = wm * TM < __builtin_amdgcn_readfirstlane(rows);
-
-    const uint16_t *aptr[CA];
-    const uint16_t *bptr[CB];
-    int alds[CA], blds[CB];
-#pragma unroll
-    for (int c = 0; c < CA; ++c) {
-        const int id = c * NT + tid, r = id >> 3, kc = (id & 7) * 8;
-        const int rr = min(r, rows - 1);
-        if (GATEUP)
-            aptr[c] = (const uint16_t *)a.A + (int64_t)a.rec_token[row0 + rr] * a.lda + kc;
-        else
-            aptr[c] = (const uint16_t *)a.A + (int64_t)(row0 + rr) * a.lda + kc;
-        alds[c] = r * LDK + kc;
-    }
-    const uint16_t *Bslot = (const uint16_t *)a.B + (int64_t)slot * a.slot_stride;
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-        const int id = c * NT + tid, r = id >> 3, kc = (id & 7) * 8;
-        const int n = min(n0 + r, N - 1);
-        bptr[c] = Bslot + (int64_t)n * K + kc;
-        blds[c] = (BM + r) * LDK + kc;
-    }
-    if (!GATEUP) {
-        for (int m = tid; m < BM; m += NT) {
-            const int rt = a.rec_route[row0 + min(m, rows - 1)];
-            s_route[m] = rt;
-            s_alpha[m] = a.topk_w[rt];
-        }
-    }
-
-    u32x4_t ra[CA], rb[CB];
-    f32x16_t acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int nk = K / BK;
-#pragma unroll
-    for (int c = 0; c < CA; ++c) ra[c] = *(const u32x4_t *)(aptr[c]);
-#pragma unroll
-    for (int c = 0; c < CB; ++c) rb[c] = *(const u32x4_t *)(bptr[c]);
-#pragma unroll
-    for (int c = 0; c < CA; ++c) *(u32x4_t *)(&lds[0][alds[c]]) = ra[c];
-#pragma unroll
-    for (int c = 0; c < CB; ++c) *(u32x4_t *)(&lds[0][blds[c]]) = rb[c];
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            const int k0 = (kt + 1) * BK;
-#pragma unroll
-            for (int c = 0; c < CA; ++c) ra[c] = *(const u32x4_t *)(aptr[c] + k0);
-#pragma unroll
-            for (int c = 0; c < CB; ++c) rb[c] = *(const u32x4_t *)(bptr[c] + k0);
-        }
-        const uint16_t *As = &lds[cur][0];
-        const uint16_t *Bs = &lds[cur][BM * LDK];
-        if (wave_active) {
-            // fragments of k16 step ks+1 are read while step ks's MFMAs run
-            bf16x8_t af[2][MI], bfr[2][NI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                af[0][i] = *(const bf16x8_t *)(As + (wm * TM + i * 32 + (lane & 31)) * LDK + (lane >> 5) * 8);
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-                bfr[0][j] = *(const bf16x8_t *)(Bs + (wn * TN + j * 32 + (lane & 31)) * LDK + (lane >> 5) * 8);
-#pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                const int cs = ks & 1;
-                if (ks + 1 < BK / 16) {
-                    const int koff = (ks + 1) * 16 + (lane >> 5) * 8;
-#pragma unroll
-                    for (int i = 0; i < MI; ++i)
-                        af[cs ^ 1][i] = *(const bf16x8_t *)(As + (wm * TM + i * 32 + (lane & 31)) * LDK + koff);
-#pragma unroll
-                    for (int j = 0; j < NI; ++j)
-                        bfr[cs ^ 1][j] = *(const bf16x8_t *)(Bs + (wn * TN + j * 32 + (lane & 31)) * LDK + koff);
-                }
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-#pragma unroll
-                    for (int j = 0; j < NI; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cs][i], bfr[cs][j], acc[i][j], 0,
-                                                                            0, 0);
-            }
-        }
-        if (kt + 1 < nk) {
-#pragma unroll
-            for (int c = 0; c < CA; ++c) *(u32x4_t *)(&lds[cur ^ 1][alds[c]]) = ra[c];
-#pragma unroll
-            for (int c = 0; c < CB; ++c) *(u32x4_t *)(&lds[cur ^ 1][blds[c]]) = rb[c];
-        }
-        __syncthreads();
-    }
-
-    if (GATEUP) {
-        uint16_t *H = (uint16_t *)a.C;
-        const int fN = N / 2;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-            for (int q = 0; q < NI / 2; ++q) {
-                const int fcol = ((n0 + wn * TN) / 64 + q) * 32 + (lane & 31);
-                if (fcol >= fN) continue;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (m < rows)
-                        H[(int64_t)(row0 + m) * a.ldc + fcol] =
-                            f32_to_bf16(silu_mul(acc[i][2 * q][r], acc[i][2 * q + 1][r]));
-                }
-            }
-        }
-    } else {
-        float *Yr = (float *)a.C;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int n = n0 + wn * TN + j * 32 + (lane & 31);
-                if (n >= N) continue;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (m < rows) Yr[(int64_t)s_route[m] * a.ldc + n] = s_alpha[m] * acc[i][j][r];
-                }
-            }
-        }
-        if (n0 == 0)
-            for (int m = tid; m < rows; m += NT) a.done[s_route[m]] = 1;
-    }
-}
-
-// ---------------------------------------------------------------------------
 // bf16 MFMA kernel with direct global->LDS loads and a ring of NS stages.
 //
-// Tile BM x BN, K step 32 (one stage = BM + BN rows of 64 bytes), 8 waves in
-// a 4 x 2 grid, each wave BM/4 x BN/2 as 32x32x16 MFMA tiles. Operand tiles
+// Tile BM x BN, K step 32 (one stage = BM + BN rows of 64 bytes), WM x WN
+// waves, each wave BM/WM x BN/WN as 32x32x16 MFMA tiles
+// (v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32 and the 8
+// consecutive k values 8*(l / 32) .. +7 of A and of B^T). Operand tiles
 // are copied straight from global memory into LDS by global_load_lds_dwordx4
 // (16 bytes per lane; one instruction fills 1 KB = 16 rows of one stage), so
 // no registers hold staged data and NS-1 stages are in flight while one is
@@ -327,6 +161,22 @@ __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Waits until at most n * STEP vector memory operations of this wave are
+// outstanding, for a run-time n in [0, MAXN].
+template <int STEP, int MAXN>
+__device__ __forceinline__ void wait_vmcnt_stages(int n)
+{
+    if constexpr (MAXN > 0) {
+        if (n >= MAXN) {
+            wait_vmcnt<MAXN * STEP>();
+            return;
+        }
+        wait_vmcnt_stages<STEP, MAXN - 1>(n);
+    } else {
+        wait_vmcnt<0>();
+    }
 }
 
 template <int BM, int BN, int NS, int WM, int WN, bool GATEUP>
@@ -529,13 +379,11 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
         // Stage 0 of this tile is complete and visible. Loads return in
-        // order, so at most the later stages' copies remain once this wave
-        // has <= (NS-2)*LOADS memory operations outstanding, even with the
-        // previous tile's output stores still in flight.
-        if (nk > 1)
-            wait_vmcnt<(NS - 2) * LOADS>();
-        else
-            wait_vmcnt<0>();
+        // order, and min(NS-2, nk-1) stages were requested after stage 0, so
+        // stage 0 is complete once no more than their copies are outstanding
+        // (operations issued later, such as the previous tile's output
+        // stores, only make the wait stricter).
+        wait_vmcnt_stages<LOADS, NS - 2>(min(NS - 2, nk - 1));
         __syncthreads();
         if (wave_active) read_frags(0, 0, 0);
 
@@ -550,10 +398,9 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
             const int stage = kt % NS;
             const bool more = kt + 1 < nk;
             if (more) {
-                if (kt + 2 < nk)
-                    wait_vmcnt<(NS - 3) * LOADS>();
-                else
-                    wait_vmcnt<0>();
+                // stage kt+1 complete: the stages requested after it are
+                // kt+2 .. min(kt+NS-2, nk-1)
+                wait_vmcnt_stages<LOADS, NS - 3>(min(NS - 3, nk - 2 - kt));
                 // A bare barrier: the stage's data is visible once every wave
                 // has waited on its own copies, and the slot refilled below was
                 // last read by fragment loads whose results fed MFMAs issued
@@ -748,15 +595,6 @@ inline unsigned grid_bound(const GemmArgs &a, int max_rows, int BM, int BN)
     return (unsigned)(mt * ntn);
 }
 
-template <int BM, int BN, int WM, int WN, bool GATEUP>
-hipError_t launch_mfma(const GemmArgs &a, int max_rows, hipStream_t st)
-{
-    const unsigned g = grid_bound(a, max_rows, BM, BN);
-    if (g == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, GATEUP>), dim3(g), dim3(WM * WN * 64), 0, st, a);
-    return hipGetLastError();
-}
-
 inline int device_cus()
 {
     static int cus = 0;
@@ -791,20 +629,11 @@ hipError_t launch_simple(const GemmArgs &a, int max_rows, hipStream_t st)
 
 }  // namespace
 
-// Kernel choice for the bf16 projections: the direct-to-LDS ring kernel
-// (tile rows, tile columns, stages, wave rows, wave columns), or with
-// MOE_REG_STAGED the register-
-// staged double-buffer kernel (rows, columns, wave grid).
-#ifndef MOE_GU_TILE
-#define MOE_GU_TILE 256, 256, 4, 4, 2
-#endif
-#ifndef MOE_DN_TILE
-#define MOE_DN_TILE 256, 256, 4, 4, 2
-#endif
-#ifdef MOE_REG_STAGED
-#define MOE_LAUNCH_MFMA launch_mfma
-#else
-#define MOE_LAUNCH_MFMA launch_mfma_lds
+// Tile shape of the ring kernel: tile rows, tile columns, stages, wave rows,
+// wave columns. (128- and 64-row tiles were measured slower than 256-row
+// tiles with idle rows, down to 64 routes per expert.)
+#ifndef MOE_RING_TILE
+#define MOE_RING_TILE 256, 256, 4, 4, 2
 #endif
 
 hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
@@ -813,7 +642,7 @@ hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, b
     if (max_rows == 0) return hipSuccess;
     if (s.dtype == MOE_DT_F32) return launch_simple<float, true>(a, max_rows, st);
     if (simple) return launch_simple<uint16_t, true>(a, max_rows, st);
-    return MOE_LAUNCH_MFMA<MOE_GU_TILE, true>(a, max_rows, st);
+    return launch_mfma_lds<MOE_RING_TILE, true>(a, max_rows, st);
 }
 
 hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
@@ -822,7 +651,7 @@ hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool
     if (max_rows == 0) return hipSuccess;
     if (s.dtype == MOE_DT_F32) return launch_simple<float, false>(a, max_rows, st);
     if (simple) return launch_simple<uint16_t, false>(a, max_rows, st);
-    return MOE_LAUNCH_MFMA<MOE_DN_TILE, false>(a, max_rows, st);
+    return launch_mfma_lds<MOE_RING_TILE, false>(a, max_rows, st);
 }
 
 }  // namespace moe
