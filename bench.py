@@ -206,17 +206,20 @@ def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
 def bench_paged(args, cfg) -> int:
     """The expert-virtualised layer: experts live in pinned host memory and
     stream into P arena slots (groups of G experts into 2 banks) on a copy
-    stream while the compute stream runs each loaded group. Reports the layer
-    throughput, the host-to-device rate, the groups and experts left out for
-    having no routes, and the bubble rate 1 - max(T_io, T_exec) / T_total
-    (T_io: busy time of the copies, T_exec: busy time of the compute kernels,
-    T_total: the layer's wall time on the compute stream)."""
+    stream while the compute stream runs each loaded group; the first banks
+    fill before routing is known. Reports the layer throughput, the
+    host-to-device rate, the experts and groups left out for having no routes,
+    the bubble rate 1 - max(T_io, T_exec) / T_total (T_io: busy time of the
+    copies, T_exec: busy time of the compute kernels, T_total: the layer's
+    wall time on the compute stream), and the max-plus model's prediction of
+    T_total from the measured service times."""
     import numpy as np
     import torch
 
     from routed_expert_ffn_top_amd import binding as B
     from routed_expert_ffn_top_amd.inputs import make_inputs
     from routed_expert_ffn_top_amd.layer import MoELayer
+    from routed_expert_ffn_top_amd.pipeline_model import predict, schedule
 
     inp = make_inputs(cfg, device="cuda", residual=False)
     layer = MoELayer(inp, paged=True)
@@ -227,16 +230,19 @@ def bench_paged(args, cfg) -> int:
         layer.forward(Y, compute=compute, copy=copy)
     torch.cuda.synchronize()
     counts = np.bincount(layer.routes["topk_idx"].cpu().numpy().ravel(), minlength=cfg.n_exp)
-    G = cfg.G
-    groups = [counts[g * G:(g + 1) * G] for g in range((cfg.n_exp + G - 1) // G)]
-    loaded_groups = sum(1 for c in groups if c.sum() > 0)
-    experts_loaded = int((counts > 0).sum())
+    G, nb = cfg.G, cfg.P // cfg.G
+    ng = (cfg.n_exp + G - 1) // G
+    routed = [int(counts[g * G:(g + 1) * G].sum()) for g in range(ng)]
+    loads = schedule(routed, nb, prefetch=True)
+    experts_copied = sum((G if ld["early"] else int((counts[ld["group"] * G:(ld["group"] + 1) * G] > 0).sum()))
+                         for ld in loads)
+    n_exec = sum(1 for r in routed if r > 0)
     expert_bytes = 3 * cfg.d * cfg.f * 2
     K = args.steps
     kernels = ["router", "topk", "route_count", "route_place", "gate_up", "down", "combine"]
-    per_step = loaded_groups + 2
+    cap = K * (n_exec + len(loads) + 2)
     for nme in kernels + ["h2d"]:
-        B.moe_profile_begin(nme, K * max(per_step, experts_loaded))
+        B.moe_profile_begin(nme, cap)
     t_total = []
     for _ in range(K):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -246,11 +252,21 @@ def bench_paged(args, cfg) -> int:
         b.synchronize()
         t_total.append(a.elapsed_time(b))
     torch.cuda.synchronize()
-    sums = {nme: sum(B.moe_profile_end(nme, K * max(per_step, experts_loaded))) / K for nme in kernels + ["h2d"]}
+    rec = {nme: B.moe_profile_end(nme, cap) for nme in kernels + ["h2d"]}
     T_total = sum(t_total) / K
-    T_io = sums["h2d"]
-    T_exec = sum(sums[n] for n in kernels)
-    h2d_bytes = experts_loaded * expert_bytes
+    T_io = sum(rec["h2d"]) / K
+    T_exec = sum(sum(rec[n]) for n in kernels) / K
+    # per-step service times, averaged over the steps: loads in loading order,
+    # executions (route count + place + gate/up + down) in group order
+    nl = len(loads)
+    L = [float(np.mean(rec["h2d"][i::nl])) for i in range(nl)]
+    cnt = np.array(rec["route_count"]).reshape(K, n_exec + 1)
+    X = [float(np.mean(cnt[:, 1 + k]) + np.mean(rec["route_place"][k::n_exec]) +
+               np.mean(rec["gate_up"][k::n_exec]) + np.mean(rec["down"][k::n_exec])) for k in range(n_exec)]
+    T_ne = float(np.mean(rec["router"]) + np.mean(rec["topk"]) + np.mean(cnt[:, 0]))
+    T_tail = float(np.mean(rec["combine"]))
+    model = predict(routed, L, X, B=nb, q=1, T_ne=T_ne, T_route=T_ne, T_tail=T_tail, prefetch=True)
+    h2d_bytes = experts_copied * expert_bytes
     gbs = h2d_bytes / (T_io / 1e3) / 1e9 if T_io > 0 else None
     out = {
         "metric": "routed tokens/s per MoE layer, experts paged from host memory (1 GPU)",
@@ -266,18 +282,22 @@ def bench_paged(args, cfg) -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, Zipf(1.1) logit bias)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "T": cfg.T, "d": cfg.d, "E": cfg.E,
-                   "k": cfg.k, "f": cfg.f, "slots": cfg.P, "G": G, "banks": cfg.P // G},
+                   "k": cfg.k, "f": cfg.f, "slots": cfg.P, "G": G, "banks": nb},
         "paging": {
-            "experts_with_routes": experts_loaded,
-            "zero_route_experts": int(cfg.n_exp - experts_loaded),
-            "groups_loaded": loaded_groups,
-            "groups_skipped": len(groups) - loaded_groups,
+            "experts_with_routes": int((counts > 0).sum()),
+            "zero_route_experts": int(cfg.n_exp - (counts > 0).sum()),
+            "groups_loaded": len(loads),
+            "groups_executed": n_exec,
+            "groups_skipped": ng - n_exec,
+            "experts_copied": experts_copied,
             "h2d_bytes_per_step": h2d_bytes,
             "t_io_ms": round(T_io, 4),
             "t_exec_ms": round(T_exec, 4),
             "t_total_ms": round(T_total, 4),
             "bubble_rate": round(1.0 - max(T_io, T_exec) / T_total, 4),
-            "kernel_ms_per_step": {n: round(v, 4) for n, v in sums.items() if n != "h2d"},
+            "maxplus_t_pipe_ms": round(model["t_pipe"], 4),
+            "maxplus_error": round(model["t_pipe"] / T_total - 1.0, 4),
+            "kernel_ms_per_step": {n: round(sum(v) / K, 4) for n, v in rec.items() if n != "h2d"},
         },
         "roofline": {
             "kernel": "host-to-device expert copies (pinned host memory to the arena)",

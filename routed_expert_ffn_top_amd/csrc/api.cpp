@@ -16,6 +16,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <deque>
 #include <mutex>
 #include <vector>
 
@@ -240,33 +241,64 @@ void arena_abort_fill(moe_arena *a, int slot)
     a->state[slot] = MOE_SLOT_AVAILABLE;
 }
 
+// Binds expert ex[i] to slot sl[i] for i < n, with loads on `st`: every slot
+// goes Filling, the stream waits for each slot's last release, the copies
+// run, and each slot's ready event is recorded and the slot published.
+// Neighbouring entries whose slots are consecutive and whose prepacked host
+// slices follow each other in memory are copied with one transfer per plane.
+// With `timed`, the copies (not the waits) are bracketed for
+// moe_profile_begin(MOE_KERNEL_H2D). Caller holds the lock.
+moe_status arena_bind_many_locked(moe_arena *a, const int *sl, const int *ex, int n, const void *const *src_gu,
+                                  const void *const *src_d, hipStream_t st, bool timed)
+{
+    const moe_shape &s = a->shape;
+    const size_t gu_bytes = (size_t)2 * s.f * s.d * a->esz, d_bytes = (size_t)s.d * s.f * a->esz;
+    for (int i = 0; i < n; ++i)
+        if (!src_gu[i] || !src_d[i]) return fail(MOE_ERR_INVALID_ARG, "bind source is NULL");
+    int reserved = 0;
+    moe_status rc = MOE_OK;
+    while (reserved < n) {
+        rc = arena_reserve(a, sl[reserved], ex[reserved]);
+        if (rc != MOE_OK) break;
+        ++reserved;
+        rc = arena_events(a, sl[reserved - 1]);
+        if (rc != MOE_OK) break;
+    }
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < n && rc == MOE_OK && e == hipSuccess; ++i)
+        if (a->last_use[sl[i]] >= 0) e = hipStreamWaitEvent(st, a->ring[a->last_use[sl[i]]], 0);
+    const int pi = (rc == MOE_OK && e == hipSuccess && timed) ? prof_begin(MOE_KERNEL_H2D, st) : -1;
+    for (int i = 0; i < n && rc == MOE_OK && e == hipSuccess;) {
+        int j = i + 1;   // extend while slots are consecutive and host slices contiguous
+        while (j < n && sl[j] == sl[j - 1] + 1 &&
+               (const char *)src_gu[j] == (const char *)src_gu[j - 1] + gu_bytes &&
+               (const char *)src_d[j] == (const char *)src_d[j - 1] + d_bytes)
+            ++j;
+        e = hipMemcpyAsync(a->plane_gu + (size_t)sl[i] * a->stride_gu * a->esz, src_gu[i],
+                           gu_bytes * (size_t)(j - i), hipMemcpyDefault, st);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(a->plane_d + (size_t)sl[i] * a->stride_d * a->esz, src_d[i],
+                               d_bytes * (size_t)(j - i), hipMemcpyDefault, st);
+        i = j;
+    }
+    if (pi >= 0) prof_end(MOE_KERNEL_H2D, pi, st);
+    for (int i = 0; i < n && rc == MOE_OK && e == hipSuccess; ++i) e = hipEventRecord(a->ready[sl[i]], st);
+    if (rc != MOE_OK || e != hipSuccess) {
+        for (int i = 0; i < reserved; ++i)
+            if (a->state[sl[i]] == MOE_SLOT_FILLING) arena_abort_fill(a, sl[i]);
+        return rc != MOE_OK ? rc : hip_fail(e, "arena bind");
+    }
+    for (int i = 0; i < n; ++i) {
+        a->ready_gen[sl[i]] += 1;
+        arena_publish_locked(a, sl[i]);
+    }
+    return MOE_OK;
+}
+
 moe_status arena_bind_locked(moe_arena *a, int slot, int expert, const void *src_gu, const void *src_d,
                              hipStream_t st)
 {
-    if (!src_gu || !src_d) return fail(MOE_ERR_INVALID_ARG, "bind source is NULL");
-    MOE_TRY(arena_reserve(a, slot, expert));
-    moe_status rc = arena_events(a, slot);
-    const moe_shape &s = a->shape;
-    const size_t gu_bytes = (size_t)2 * s.f * s.d * a->esz, d_bytes = (size_t)s.d * s.f * a->esz;
-    hipError_t e = hipSuccess;
-    if (rc == MOE_OK && a->last_use[slot] >= 0) e = hipStreamWaitEvent(st, a->ring[a->last_use[slot]], 0);
-    if (rc == MOE_OK && e == hipSuccess)
-        e = TIMED(MOE_KERNEL_H2D, st, [&]() {
-            hipError_t r = hipMemcpyAsync(a->plane_gu + (size_t)slot * a->stride_gu * a->esz, src_gu, gu_bytes,
-                                          hipMemcpyDefault, st);
-            if (r == hipSuccess)
-                r = hipMemcpyAsync(a->plane_d + (size_t)slot * a->stride_d * a->esz, src_d, d_bytes,
-                                   hipMemcpyDefault, st);
-            return r;
-        }());
-    if (rc == MOE_OK && e == hipSuccess) e = hipEventRecord(a->ready[slot], st);
-    if (rc != MOE_OK || e != hipSuccess) {
-        arena_abort_fill(a, slot);
-        return rc != MOE_OK ? rc : hip_fail(e, "arena_bind_slot");
-    }
-    a->ready_gen[slot] += 1;
-    arena_publish_locked(a, slot);
-    return MOE_OK;
+    return arena_bind_many_locked(a, &slot, &expert, 1, &src_gu, &src_d, st, true);
 }
 
 // Checks phi against the arena, makes `st` wait for each named slot's load.
@@ -684,15 +716,16 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
     const int kp = s.k + s.n_shared, ne = s.E + s.n_shared;
     hipStream_t cs = S(compute), ps = copy ? S(copy) : cs;
     const float *L = logits;
-    if (W_r) {
-        L = ws_at<float>(ws, w.logits);
-        HIP_TRY(TIMED(MOE_KERNEL_ROUTER, cs, launch_router_logits(s, X, W_r, bias, ws_at<float>(ws, w.logits), cs)),
-                "router launch");
-    }
     std::vector<int32_t> phi(kMaxExp, -1);
     PhiArg pa;
 
     if (!host_gu) {
+        if (W_r) {
+            L = ws_at<float>(ws, w.logits);
+            HIP_TRY(TIMED(MOE_KERNEL_ROUTER, cs,
+                          launch_router_logits(s, X, W_r, bias, ws_at<float>(ws, w.logits), cs)),
+                    "router launch");
+        }
         // Resident layer: every expert must be Ready in the arena.
         MOE_TRY(arena_phi(arena, phi.data(), ne));
         for (int e = 0; e < ne; ++e)
@@ -713,16 +746,52 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
         return MOE_OK;
     }
 
-    // Paged layer (sections 3.3-3.4): route once, read the per-expert route
-    // counts (the one host synchronization), then stream the groups that have
-    // routes through the banks: group g of G experts (expert e is member
-    // r(e) = e mod G of group e / G; the permutation pi is the identity) goes
-    // to bank b = (sequence number mod B), slots b*G + r(e) (Eq. 4). Loads run
-    // on the copy stream, each after the bank's previous release; each group's
-    // route build and expert FFN run on the compute stream after the load.
+    // Paged layer (sections 3.3-3.4). Group g holds experts g*G .. g*G+G-1
+    // (expert e is member r(e) = e mod G; the permutation pi is the
+    // identity), and a group loaded into bank b occupies slots b*G + r(e)
+    // (Eq. 4). The first B groups are loaded in group order before routing is
+    // known, while the router and top-k run; then the per-expert route counts
+    // are read back (the one host synchronisation), groups with no routes are
+    // skipped (a prefetched one just frees its bank), and each later group
+    // with routes is loaded into the bank released longest ago, only its
+    // experts with routes. Loads run on the copy stream, each after its
+    // bank's previous release; each group's route build and expert FFN run on
+    // the compute stream after its load.
     if ((int64_t)s.T * kp > s.capacity)
         return fail(MOE_ERR_CAPACITY, "paging needs capacity >= T*K' (%lld)", (long long)s.T * kp);
+    for (int e = 0; e < ne; ++e)
+        if (!host_gu[e] || !host_d[e]) return fail(MOE_ERR_INVALID_ARG, "host expert %d pointer is NULL", e);
     const int G = arena->G, B = s.P / G;
+    const int ngroups = (ne + G - 1) / G;
+    const int npre = std::min(B, ngroups);
+    std::lock_guard<std::mutex> lk(arena->mu);
+    for (int sl = 0; sl < s.P; ++sl) {  // forget the previous layer's mapping
+        if (arena->owner[sl] >= 0) arena->slot_of[arena->owner[sl]] = -1;
+        arena->owner[sl] = -1;
+        arena->state[sl] = MOE_SLOT_AVAILABLE;
+    }
+    std::vector<int> bsl, bex;
+    std::vector<const void *> bgu, bd;
+    auto bind_group = [&](int g, int bank, const int32_t *counts) -> moe_status {
+        bsl.clear(); bex.clear(); bgu.clear(); bd.clear();
+        for (int e = g * G; e < std::min(ne, (g + 1) * G); ++e) {
+            if (counts && counts[e] == 0) continue;
+            bsl.push_back(bank * G + (e % G));
+            bex.push_back(e);
+            bgu.push_back(host_gu[e]);
+            bd.push_back(host_d[e]);
+        }
+        return arena_bind_many_locked(arena, bsl.data(), bex.data(), (int)bsl.size(), bgu.data(), bd.data(), ps,
+                                      true);
+    };
+    if (ps != cs) {  // prefetch needs its own copy stream to overlap routing
+        for (int g = 0; g < npre; ++g) MOE_TRY(bind_group(g, g, nullptr));
+    }
+    if (W_r) {
+        L = ws_at<float>(ws, w.logits);
+        HIP_TRY(TIMED(MOE_KERNEL_ROUTER, cs, launch_router_logits(s, X, W_r, bias, ws_at<float>(ws, w.logits), cs)),
+                "router launch");
+    }
     HIP_TRY(TIMED(MOE_KERNEL_TOPK, cs,
                   launch_topk(s, 0, s.T, L, routes->topk_idx, routes->topk_w, ws_at<int32_t>(ws, w.done), cs)),
             "top-k launch");
@@ -733,33 +802,35 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
     HIP_TRY(hipMemcpyAsync(ecount.data(), ws_at<int32_t>(ws, w.ecount), ne * 4, hipMemcpyDeviceToHost, cs),
             "hipMemcpyAsync");
     HIP_TRY(hipStreamSynchronize(cs), "hipStreamSynchronize");
-    for (int e = 0; e < ne; ++e)
-        if (!host_gu[e] || !host_d[e]) return fail(MOE_ERR_INVALID_ARG, "host expert %d pointer is NULL", e);
-    std::lock_guard<std::mutex> lk(arena->mu);
-    for (int sl = 0; sl < s.P; ++sl) {  // forget the previous layer's mapping
-        if (arena->owner[sl] >= 0) arena->slot_of[arena->owner[sl]] = -1;
-        arena->owner[sl] = -1;
-        arena->state[sl] = MOE_SLOT_AVAILABLE;
-    }
-    const int ngroups = (ne + G - 1) / G;
-    int seq = 0;
+    const bool prefetched = ps != cs;
+    std::deque<int> banks;  // free or released banks, least recently used first
+    if (!prefetched)
+        for (int b = 0; b < B; ++b) banks.push_back(b);
     for (int g = 0; g < ngroups; ++g) {
         int routed = 0;
         for (int e = g * G; e < std::min(ne, (g + 1) * G); ++e) routed += ecount[e];
-        if (routed == 0) continue;  // a group with no routes is never loaded
-        const int b = seq++ % B;
-        std::fill(phi.begin(), phi.end(), -1);
-        for (int e = g * G; e < std::min(ne, (g + 1) * G); ++e) {
-            if (ecount[e] == 0) continue;
-            const int slot = b * G + (e % G);
-            MOE_TRY(arena_bind_locked(arena, slot, e, host_gu[e], host_d[e], ps));
-            phi[e] = slot;
+        const bool pre = prefetched && g < npre;
+        if (routed == 0) {  // never loaded, or loaded for nothing: its bank is free now
+            if (pre) banks.push_front(g);
+            continue;
         }
+        int bank;
+        if (pre) {
+            bank = g;
+        } else {
+            bank = banks.front();
+            banks.pop_front();
+            MOE_TRY(bind_group(g, bank, ecount.data()));
+        }
+        std::fill(phi.begin(), phi.end(), -1);
+        for (int e = g * G; e < std::min(ne, (g + 1) * G); ++e)
+            if (ecount[e] > 0) phi[e] = bank * G + (e % G);
         MOE_TRY(check_phi(shape, phi.data(), &pa));
         MOE_TRY(arena_acquire(arena, phi.data(), cs));
         MOE_TRY(route_build_impl(s, w, 0, s.T, nullptr, pa, 0, *routes, ws, cs));
         MOE_TRY(experts_impl(s, w, X, *routes, arena, s.T * kp, false, ws, cs));
         MOE_TRY(arena_release_after(arena, phi.data(), cs));
+        banks.push_back(bank);
     }
     HIP_TRY(TIMED(MOE_KERNEL_COMBINE, cs, launch_combine(s, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), cs)),
                 "combine launch");

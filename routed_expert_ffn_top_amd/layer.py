@@ -50,16 +50,17 @@ class MoELayer:
         Wu = inp.Wu.to(self.device)
         Wd = inp.Wd.to(self.device)
         if paged:
-            self.host_gu, self.host_d = [], []
+            # prepacked experts in two pinned host planes, expert after expert,
+            # so that consecutive experts load with one transfer per plane
+            self.host_gu_plane = torch.empty((ne, 2 * cfg.f, cfg.d), dtype=Wg.dtype, pin_memory=True)
+            self.host_d_plane = torch.empty((ne, cfg.d, cfg.f), dtype=Wd.dtype, pin_memory=True)
             tmp = torch.empty((2 * cfg.f, cfg.d), dtype=Wg.dtype, device=self.device)
             for e in range(ne):
                 B.moe_pack_gate_up(self.shape, Wg[e], Wu[e], tmp, 1, 0, 0, stream)
-                gu = torch.empty(tmp.shape, dtype=tmp.dtype, pin_memory=True)
-                gu.copy_(tmp)
-                dn = torch.empty(Wd[e].shape, dtype=Wd.dtype, pin_memory=True)
-                dn.copy_(Wd[e])
-                self.host_gu.append(gu)
-                self.host_d.append(dn)
+                self.host_gu_plane[e].copy_(tmp)
+                self.host_d_plane[e].copy_(Wd[e])
+            self.host_gu = [self.host_gu_plane[e] for e in range(ne)]
+            self.host_d = [self.host_d_plane[e] for e in range(ne)]
             self.phi = None
         else:
             self.phi = list(range(ne)) if phi is None else [int(x) for x in phi]
