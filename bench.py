@@ -203,7 +203,7 @@ def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
                           f"for {n} sampled tokens ({t_ffn:.2f} s), extrapolated to T={cfg.T}"))}
 
 
-def bench_paged(args, cfg) -> int:
+def run_paged(args, cfg):
     """The expert-virtualised layer: experts live in pinned host memory and
     stream into P arena slots (groups of G experts into 2 banks) on a copy
     stream while the compute stream runs each loaded group; the first banks
@@ -221,6 +221,8 @@ def bench_paged(args, cfg) -> int:
     from routed_expert_ffn_top_amd.layer import MoELayer
     from routed_expert_ffn_top_amd.pipeline_model import predict, schedule
 
+    if getattr(args, "group_size", None):
+        cfg = cfg.with_(G=args.group_size)
     inp = make_inputs(cfg, device="cuda", residual=False)
     layer = MoELayer(inp, paged=True)
     Y = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
@@ -309,7 +311,48 @@ def bench_paged(args, cfg) -> int:
             "traffic": h2d_bytes,
         },
     }
+    profile = {"routed": routed, "group_size": [min(G, cfg.n_exp - g * G) for g in range(ng)],
+               "routed_experts": [int((counts[g * G:(g + 1) * G] > 0).sum()) for g in range(ng)],
+               "l_expert": T_io / experts_copied, "X": X, "T_ne": T_ne, "T_tail": T_tail}
+    layer.close()
+    return out, profile
+
+
+def bench_paged(args, cfg) -> int:
+    out, _ = run_paged(args, cfg)
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_configure(args, cfg, sizes=(1, 2, 4, 8, 16)) -> int:
+    """The configuration step of the pages (section 3.4) on this GPU: one
+    profiled run of the paged layer per group size g (with B = P/g banks),
+    then the max-plus model evaluates every feasible bank count per g under
+    the arena's slot budget P and picks (G*, B*). Prints the measured layer
+    time of each profiled run next to its prediction, and the choice."""
+    from routed_expert_ffn_top_amd.pipeline_model import configure, predict_from_profile
+
+    profiles, measured = {}, {}
+    for g in sizes:
+        if cfg.P % g:
+            continue
+        args.group_size = g
+        out, prof = run_paged(args, cfg)
+        profiles[g] = prof
+        measured[g] = out["paging"]["t_total_ms"]
+        print(f"profiled G={g}: {measured[g]:.3f} ms", file=sys.stderr, flush=True)
+    res = configure(profiles, cfg.P)
+    rows = [{"G": g, "B": cfg.P // g, "measured_ms": round(measured[g], 4),
+             "predicted_ms": round(predict_from_profile(profiles[g], cfg.P // g)["t_pipe"], 4)}
+            for g in sorted(profiles)]
+    print(json.dumps({
+        "metric": "paged layer configuration (max-plus model over profiled group sizes)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "T": cfg.T, "slots": cfg.P},
+        "profiled_runs": rows,
+        "chosen": {"G": res["G"], "B": res["B"], "predicted_ms": round(res["t_pipe"], 4),
+                   "measured_ms_at_G": round(measured[res["G"]], 4)},
+        "predicted_ms_by_G_B": {f"{g}x{b}": round(t, 4) for (g, b), t in sorted(res["table"].items())},
+    }), flush=True)
     return 0
 
 
@@ -377,6 +420,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="olmoe_t4096", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--group-size", type=int, default=None, help="paged workloads: experts per group")
+    ap.add_argument("--configure", action="store_true",
+                    help="paged workloads: profile every group size and pick (G, B) with the max-plus model")
     ap.add_argument("--no-context", action="store_true", help="skip the torch.matmul ceiling")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for HBM counter calibration)")
@@ -418,6 +464,8 @@ def main() -> int:
 
     B.load()
     if args.workload.startswith("virt_"):
+        if args.configure:
+            return bench_configure(args, CONFIGS[args.workload])
         return bench_paged(args, CONFIGS[args.workload])
     if args.workload.startswith("mixtral_stack_"):
         return bench_stack(args, CONFIGS[args.workload.replace("mixtral_stack_", "mixtral_")])

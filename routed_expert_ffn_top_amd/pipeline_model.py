@@ -110,3 +110,37 @@ def predict(routed: Sequence[int], L: Sequence[float], X: Sequence[float], B: in
     return {"t_pipe": t_pipe, "t_io": t_io, "t_exec": t_exec,
             "bubble": 1.0 - max(t_io, t_exec) / t_pipe if t_pipe > 0 else 0.0,
             "loads": len(loads)}
+
+
+def predict_from_profile(prof: dict, b: int) -> dict:
+    """Prediction for bank count b from one profiled run at group size g:
+    prof = {routed: per-group route counts, experts: per-group expert ids
+    with routes (counts), g, l_expert: load time per expert, X: execution
+    time per executed group (group order), T_ne, T_tail}. A load copies every
+    expert of its group when issued before routing, else only the experts
+    with routes."""
+    loads = schedule(prof["routed"], b, prefetch=True)
+    L = [prof["l_expert"] * (prof["group_size"][ld["group"]] if ld["early"] else prof["routed_experts"][ld["group"]])
+         for ld in loads]
+    return predict(prof["routed"], L, prof["X"], B=b, q=1, T_ne=prof["T_ne"], T_route=prof["T_ne"],
+                   T_tail=prof["T_tail"], prefetch=True)
+
+
+def configure(profiles: Dict[int, dict], max_slots: int) -> dict:
+    """The nested search of the pages' configuration step: for every profiled
+    group size g, the bank counts b with g*b <= max_slots (the arena's memory
+    budget) are evaluated with the max-plus model and the best b kept (inner
+    optimisation); the group size whose best configuration predicts the
+    shortest layer wins (outer optimisation)."""
+    table = {}
+    best = None
+    for g, prof in sorted(profiles.items()):
+        inner = None
+        for b in range(1, max_slots // g + 1):
+            t = predict_from_profile(prof, b)["t_pipe"]
+            table[(g, b)] = t
+            if inner is None or t < inner[1] - 1e-12:
+                inner = (b, t)
+        if inner is not None and (best is None or inner[1] < best[2] - 1e-12):
+            best = (g, inner[0], inner[1])
+    return {"G": best[0], "B": best[1], "t_pipe": best[2], "table": table}

@@ -53,3 +53,27 @@ def test_empty_groups():
     assert r["t_pipe"] == pytest.approx(2 + 2 + 2 + 2 + 1)
     s = schedule([0, 0, 3], B=2, prefetch=False)
     assert [(x["group"], x["bank"]) for x in s] == [(2, 0)]
+
+
+def _profile(g, n_exp, l_e, x_per_group, T_ne=0.0):
+    ng = n_exp // g
+    return {"routed": [1] * ng, "group_size": [g] * ng, "routed_experts": [g] * ng, "l_expert": l_e,
+            "X": [x_per_group] * ng, "T_ne": T_ne, "T_tail": 0.0}
+
+
+def test_configure_prefers_overlap_within_budget():
+    from routed_expert_ffn_top_amd.pipeline_model import configure
+    # 16 experts, load 1 per expert, execution 3 per group whatever its size:
+    # one big group cannot overlap anything; many small groups overlap loads
+    # with execution but pay the per-group execution time more often
+    profiles = {16: _profile(16, 16, 1.0, 3.0), 4: _profile(4, 16, 1.0, 3.0), 1: _profile(1, 16, 1.0, 3.0)}
+    res = configure(profiles, max_slots=16)
+    t = res["table"]
+    assert t[(16, 1)] == pytest.approx(16 + 3)            # load everything, then run
+    assert t[(4, 1)] == pytest.approx(4 * (4 + 3))        # one bank: no overlap
+    assert t[(4, 2)] == pytest.approx(4 + 4 + 4 + 4 + 3)  # two banks: loads back to back
+    assert t[(1, 16)] == pytest.approx(1 + 16 * 3)        # execution-bound
+    assert (res["G"], res["B"]) == (4, 2) and res["t_pipe"] == pytest.approx(19.0)
+    # a budget of 4 slots rules out g = 16 and leaves g = 4 with one bank
+    res = configure(profiles, max_slots=4)
+    assert (16, 1) not in res["table"] and res["G"] in (1, 4)
