@@ -143,7 +143,8 @@ moe_status moe_last_error(char *buf, size_t n);
  * Bytes of device workspace the calls need for this shape. The workspace
  * holds the device error word, per-block route counts and ranks, the router
  * logits, the SwiGLU intermediate H [C][f] and the per-route fp32 output rows
- * Yr [T*K'][d], plus the per-route "computed" marks. One workspace belongs to
+ * Yr [S][T*K'][d] (S partial sums over f, see moe_expert_ffn), plus the
+ * per-route "computed" marks. One workspace belongs to
  * one layer invocation at a time; it must persist from moe_route_build to
  * the finalizing moe_expert_ffn. Returns 0 for an invalid shape.
  */
@@ -224,9 +225,13 @@ moe_status moe_route_build(const moe_shape *shape, int32_t t0, int32_t nt,
  * MOE_FFN_EXPERTS: for each record p of slot s, H[p] = SiLU(g) * u with
  * (g, u) = X[rec_token[p]] times slot s's gate/up slice, then
  * Yr[rec_route[p]] = alpha * (H[p] times slot s's down slice); the route is
- * marked computed. MOE_FFN_FINALIZE: for every token, Y[t] += Yr[t*K'+j] for
- * j = 0..K'-1 in ascending order over the computed routes. The sum order is
- * fixed, so Y is bitwise run-to-run identical and independent of phi and P.
+ * marked computed. When the down tiles alone would leave the GPU idle (few
+ * routes per expert), the down projection's K = f is split into S equal
+ * ranges and each route gets S partial rows (S depends only on the shape).
+ * MOE_FFN_FINALIZE: for every token, Y[t] += Yr[t*K'+j] for j = 0..K'-1 in
+ * ascending order over the computed routes (each route's partial rows in
+ * ascending order). The sum order is fixed, so Y is bitwise run-to-run
+ * identical and independent of phi and P.
  * arena and phi may be NULL when only MOE_FFN_FINALIZE is set.
  */
 moe_status moe_expert_ffn(const moe_shape *shape, const void *X, float *Y,

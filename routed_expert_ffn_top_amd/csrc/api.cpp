@@ -379,6 +379,7 @@ GemmArgs gemm_args(const moe_shape &s, const moe_routes &r, const moe_arena *a)
     g.rec_token = r.rec_token;
     g.rec_route = r.rec_route;
     g.topk_w = r.topk_w;
+    g.splits = 1;
     (void)a;
     return g;
 }
@@ -406,6 +407,8 @@ moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, co
     h.C = ws_at<float>(ws, w.Yr);
     h.ldc = s.d;
     h.done = ws_at<int32_t>(ws, w.done);
+    h.splits = down_splits(s);
+    h.split_stride = (int64_t)s.T * (s.k + s.n_shared) * s.d;
     HIP_TRY(TIMED(MOE_KERNEL_DOWN, st, launch_down(s, h, max_rows, simple, st)), "down launch");
     return MOE_OK;
 }

@@ -5,9 +5,10 @@
 //
 // Combine: Y holds A_t on entry. Each thread owns 4 consecutive columns of
 // one token row and adds the token's computed route rows Yr[t*K' + j] in
-// ascending j, so the fp32 sum order is fixed: no atomics, bitwise
-// reproducible, and independent of how routes were spread over slots,
-// workgroups or invocations.
+// ascending j (each route's S partial rows, when the down projection splits
+// its K, in ascending split order), so the fp32 sum order is fixed: no
+// atomics, bitwise reproducible, and independent of how routes were spread
+// over slots, workgroups or invocations.
 #include "common.h"
 
 namespace moe {
@@ -15,7 +16,8 @@ namespace {
 
 __global__ __launch_bounds__(256) void k_combine(float *__restrict__ Y, int64_t ldy,
                                                  const float *__restrict__ Yr,
-                                                 const int32_t *__restrict__ done, int d, int kp)
+                                                 const int32_t *__restrict__ done, int d, int kp,
+                                                 int splits, int64_t split_stride)
 {
     const int t = blockIdx.y;
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -24,11 +26,13 @@ __global__ __launch_bounds__(256) void k_combine(float *__restrict__ Y, int64_t 
     for (int j = 0; j < kp; ++j) {
         const int64_t i = (int64_t)t * kp + j;
         if (done[i]) {
-            const float4 v = *(const float4 *)(Yr + i * d + c);
-            y.x += v.x;
-            y.y += v.y;
-            y.z += v.z;
-            y.w += v.w;
+            for (int q = 0; q < splits; ++q) {   // route j's partial rows, in order
+                const float4 v = *(const float4 *)(Yr + q * split_stride + i * d + c);
+                y.x += v.x;
+                y.y += v.y;
+                y.z += v.z;
+                y.w += v.w;
+            }
         }
     }
     *(float4 *)(Y + (int64_t)t * ldy + c) = y;
@@ -89,7 +93,7 @@ hipError_t launch_combine(const moe_shape &s, float *Y, const float *Yr, const i
     if (s.T == 0) return hipSuccess;
     const dim3 grid((unsigned)((s.d / 4 + 255) / 256), (unsigned)s.T);
     hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, Y, s.ldy, Yr, done, s.d,
-                       s.k + s.n_shared);
+                       s.k + s.n_shared, down_splits(s), (int64_t)s.T * (s.k + s.n_shared) * s.d);
     return hipGetLastError();
 }
 

@@ -26,12 +26,28 @@ struct WsLayout {
     size_t done;     // int32[T*K']: 1 once route i's Yr row is computed
     size_t logits;   // float[T][E]
     size_t H;        // dtype[C][f]
-    size_t Yr;       // float[T*K'][d]
+    size_t Yr;       // float[S][T*K'][d], S = down_splits (partial sums over f)
     size_t total;
     int nblk;        // ceil(C / kRouteBlock)
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Splits of the down projection's K = f: when the down tiles (about
+// experts x row blocks x d/256) would not fill the GPU, each tile's K range
+// is cut in S pieces whose partial products go to S separate per-route rows,
+// summed in fixed order by the combine. S doubles while the tile count stays
+// <= 512 and f splits into multiples of 64; at most 4.
+inline int down_splits(const moe_shape &s)
+{
+    if (s.dtype != MOE_DT_BF16) return 1;
+    const int64_t ne = s.E + s.n_shared;
+    const int64_t per = ((int64_t)s.T * (s.k + s.n_shared) + ne - 1) / ne;
+    const int64_t tiles = ne * ((per + 255) / 256) * ((s.d + 255) / 256);
+    int S = 1;
+    while (S < 4 && tiles * S * 2 <= 512 && (s.f % (64 * S * 2)) == 0) S *= 2;
+    return S;
+}
 
 inline WsLayout ws_layout(const moe_shape &s)
 {
@@ -47,7 +63,7 @@ inline WsLayout ws_layout(const moe_shape &s)
     w.done = o;   o = align_up(o + (size_t)s.T * kp * 4, 256);
     w.logits = o; o = align_up(o + (size_t)s.T * s.E * 4, 256);
     w.H = o;      o = align_up(o + (size_t)s.capacity * s.f * esz, 256);
-    w.Yr = o;     o = align_up(o + (size_t)s.T * kp * s.d * 4, 256);
+    w.Yr = o;     o = align_up(o + (size_t)down_splits(s) * s.T * kp * s.d * 4, 256);
     w.total = o;
     return w;
 }
@@ -68,6 +84,8 @@ struct GemmArgs {
     int N, K;
     void *C;                     // H (gate/up) or Yr (down)
     int64_t ldc;                 // f or d
+    int splits;                  // K split in this many equal ranges (down)
+    int64_t split_stride;        // elements between the partial outputs
     const float *topk_w;         // down: weight of route i
     int32_t *done;               // down: computed marks
 };
@@ -89,7 +107,7 @@ hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, b
 hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
                        hipStream_t st);
 hipError_t launch_combine(const moe_shape &s, float *Y, const float *Yr, const int32_t *done,
-                          hipStream_t st);
+                          hipStream_t st);   // sums the down_splits(s) partial rows of each route
 hipError_t launch_pack_gate_up(const moe_shape &s, const void *Wg, const void *Wu, void *dst,
                                int n, int64_t src_stride, int64_t dst_stride, hipStream_t st);
 hipError_t launch_selftest_mfma(float *out, hipStream_t st);

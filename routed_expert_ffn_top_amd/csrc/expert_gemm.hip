@@ -33,7 +33,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct TileInfo {
-    int slot, row0, rows, n0;
+    int slot, row0, rows, n0, ks;   // ks: which of the a.splits K ranges
 };
 
 __device__ __forceinline__ int wave_incl_scan(int v, int lane)
@@ -68,7 +68,7 @@ __device__ bool find_tile(const GemmArgs &a, TileInfo *ti)
         for (int s0 = 0; s0 < a.P; s0 += 64) {
             const int s = s0 + lane;
             const int cnt = s < a.P ? a.slot_offset[s + 1] - a.slot_offset[s] : 0;
-            const int w = (cnt + BM - 1) / BM * ntn;
+            const int w = (cnt + BM - 1) / BM * ntn * a.splits;
             total += __shfl(wave_incl_scan(w, lane), 63, 64);
         }
         const int bid = blockIdx.x;
@@ -80,16 +80,17 @@ __device__ bool find_tile(const GemmArgs &a, TileInfo *ti)
                 const int s = s0 + lane;
                 const int cnt = s < a.P ? a.slot_offset[s + 1] - a.slot_offset[s] : 0;
                 const int mt = (cnt + BM - 1) / BM;
-                const int w = mt * ntn;
+                const int w = mt * ntn * a.splits;
                 const int inc = wave_incl_scan(w, lane);
                 const int ex = run + inc - w;
                 if (s < a.P && w > 0 && L >= ex && L < ex + w) {
                     const int local = L - ex;
-                    const int nt = local / mt, ml = local % mt;
+                    const int ml = local % mt, rest = local / mt;
                     ti->slot = s;
                     ti->row0 = a.slot_offset[s] + ml * BM;
                     ti->rows = min(BM, cnt - ml * BM);
-                    ti->n0 = nt * BN;
+                    ti->ks = rest % a.splits;
+                    ti->n0 = (rest / a.splits) * BN;
                 }
                 run += __shfl(inc, 63, 64);
             }
@@ -203,6 +204,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int K = a.K, N = a.N;
+    const int Kc = K / a.splits;   // each tile's K range: [ks * Kc, (ks + 1) * Kc)
     const int P = a.P;
     const int ntn = (N + BN - 1) / BN;
 
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
             const int s = s0 + lane;
             const int off = s < P ? a.slot_offset[s] : 0;
             const int cnt = s < P ? a.slot_offset[s + 1] - off : 0;
-            const int w = (cnt + BM - 1) / BM * ntn;
+            const int w = (cnt + BM - 1) / BM * ntn * a.splits;
             const int inc = wave_incl_scan(w, lane);
             if (s < P) {
                 s_tpref[s] = run + inc - w;
@@ -252,7 +254,8 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         t.slot = lo;
         t.row0 = s_off[lo] + ml * BM;
         t.rows = __builtin_amdgcn_readfirstlane(min(BM, cnt_s - ml * BM));
-        t.n0 = (local / mt) * BN;
+        t.ks = (local / mt) % a.splits;
+        t.n0 = (local / mt / a.splits) * BN;
         return t;
     };
 
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         for (int j = 0; j < AI; ++j) {
             const int r = (wave * AI + j) * 16 + lr;
             const int c = lp ^ ((r >> 2) & 3);
-            asrc[j] = (const char *)a.A + ((int64_t)rows[j] * a.lda) * 2 + c * 16;
+            asrc[j] = (const char *)a.A + ((int64_t)rows[j] * a.lda + (int64_t)t.ks * Kc) * 2 + c * 16;
         }
         const char *Bslot = (const char *)a.B + (int64_t)t.slot * a.slot_stride * 2;
 #pragma unroll
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
             const int r = (wave * BI + j) * 16 + lr;
             const int c = lp ^ ((r >> 2) & 3);
             const int n = min(t.n0 + r, N - 1);
-            bsrc[j] = Bslot + (int64_t)n * K * 2 + c * 16;
+            bsrc[j] = Bslot + ((int64_t)n * K + (int64_t)t.ks * Kc) * 2 + c * 16;
         }
     };
     // down: route id and alpha of tile row tid (threads tid < BM), staged in
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
     };
 
-    const int nk = K / BK;
+    const int nk = Kc / BK;
     int tl = li, par = 0;
     TileInfo cur = decode(start_x + tl);
     int32_t rows[AI];
@@ -469,7 +472,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                 }
             }
         } else {
-            float *Yr = (float *)a.C;
+            float *Yr = (float *)a.C + cur.ks * a.split_stride;
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                     }
                 }
             }
-            if (cur.n0 == 0)
+            if (cur.n0 == 0 && cur.ks == 0)
                 for (int m = tid; m < cur.rows; m += NT) a.done[s_route[par][m]] = 1;
         }
         if (!has_next) break;
@@ -517,7 +520,8 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a)
     if (!find_tile<BM, BN>(a, &ti)) return;
     const int slot = ti.slot, row0 = ti.row0, rows = ti.rows, n0 = ti.n0;
     const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    const int K = a.K, N = a.N;
+    const int K = a.K / a.splits, N = a.N;   // this tile's K range: [kb, kb + K)
+    const int64_t kb = (int64_t)ti.ks * K;
 
     int col[4];
 #pragma unroll
@@ -525,9 +529,9 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a)
 
     const int lr = tid >> 2, lk = (tid & 3) * 4;
     const int rr = min(lr, rows - 1);
-    const TE *ap = GATEUP ? (const TE *)a.A + (int64_t)a.rec_token[row0 + rr] * a.lda
-                          : (const TE *)a.A + (int64_t)(row0 + rr) * a.lda;
-    const TE *bp = (const TE *)a.B + (int64_t)slot * a.slot_stride + (int64_t)min(n0 + lr, N - 1) * K;
+    const TE *ap = (GATEUP ? (const TE *)a.A + (int64_t)a.rec_token[row0 + rr] * a.lda
+                           : (const TE *)a.A + (int64_t)(row0 + rr) * a.lda) + kb;
+    const TE *bp = (const TE *)a.B + (int64_t)slot * a.slot_stride + (int64_t)min(n0 + lr, N - 1) * a.K + kb;
     if (!GATEUP && tid < BM) {
         const int rt = a.rec_route[row0 + min(tid, rows - 1)];
         s_route[tid] = rt;
@@ -576,7 +580,7 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a)
                     st_from_f32<TE>(H + (int64_t)(row0 + m) * a.ldc + fcol, silu_mul(acc[i][j], acc[i][j + 2]));
             }
         } else {
-            float *Yr = (float *)a.C;
+            float *Yr = (float *)a.C + ti.ks * a.split_stride;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = n0 + col[j];
@@ -584,15 +588,16 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a)
             }
         }
     }
-    if (!GATEUP && n0 == 0 && tid < rows) a.done[s_route[tid]] = 1;
+    if (!GATEUP && n0 == 0 && ti.ks == 0 && tid < rows) a.done[s_route[tid]] = 1;
 }
 
-// Upper bound of tiles: sum over slots of ceil(c_s / BM) <= ceil(R / BM) + P.
+// Upper bound of tiles: sum over slots of ceil(c_s / BM) <= ceil(R / BM) + P,
+// times the column blocks and the K splits.
 inline unsigned grid_bound(const GemmArgs &a, int max_rows, int BM, int BN)
 {
     const int64_t mt = (max_rows + BM - 1) / BM + a.P;
     const int64_t ntn = (a.N + BN - 1) / BN;
-    return (unsigned)(mt * ntn);
+    return (unsigned)(mt * ntn * a.splits);
 }
 
 inline int device_cus()
