@@ -168,6 +168,30 @@ def torch_matmul_ceiling(torch, n=8192, reps=10) -> float:
     return 2.0 * n ** 3 * reps / (s.elapsed_time(e) / 1e3) / 1e12
 
 
+def torch_bmm_expert_shape(torch, cfg, reps=10) -> dict:
+    """The vendor library (torch.bmm on hipBLASLt) on the dense batched
+    equivalent of the two projections: every expert gets exactly the mean
+    number of rows, with no gather, no scatter and no SwiGLU."""
+    m = cfg.T * cfg.kp // cfg.n_exp
+    out = {}
+    for name, n, k in (("gate_up", 2 * cfg.f, cfg.d), ("down", cfg.d, cfg.f)):
+        a = torch.randn((cfg.n_exp, m, k), device="cuda", dtype=torch.bfloat16)
+        b = (torch.randn((cfg.n_exp, k, n), device="cuda", dtype=torch.bfloat16) * 0.02).contiguous()
+        for _ in range(3):
+            torch.bmm(a, b)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            torch.bmm(a, b)
+        e.record()
+        torch.cuda.synchronize()
+        out[f"torch_bmm_{name}_{cfg.n_exp}x{m}x{n}x{k}_tflops"] = round(
+            2.0 * cfg.n_exp * m * n * k * reps / (s.elapsed_time(e) / 1e3) / 1e12, 1)
+        del a, b
+    return out
+
+
 def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
     """The CPU oracle (as it stands) on the same workload: routing for every
     token, the expert FFN on a token sample sized to ~target_s seconds,
@@ -552,7 +576,8 @@ def main() -> int:
         },
     }
     if not args.no_context:
-        out["context"] = {"torch_matmul_bf16_8192_tflops": round(torch_matmul_ceiling(torch), 1)}
+        out["context"] = {"torch_matmul_bf16_8192_tflops": round(torch_matmul_ceiling(torch), 1),
+                          **torch_bmm_expert_shape(torch, cfg)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, cfg)
     else:
