@@ -22,6 +22,7 @@
 // logical tile index is remapped to give each XCD one contiguous range of
 // tiles: the sharing happens in that XCD's own L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -178,6 +179,16 @@ __device__ __forceinline__ void wait_vmcnt_stages(int n)
     } else {
         wait_vmcnt<0>();
     }
+}
+
+// Two floats rounded to bf16 (nearest even) and packed, lo in bits 15:0
+// (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <int BM, int BN, int NS, int WM, int WN, bool GATEUP>
@@ -385,7 +396,9 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         // order, and min(NS-2, nk-1) stages were requested after stage 0, so
         // stage 0 is complete once no more than their copies are outstanding
         // (operations issued later, such as the previous tile's output
-        // stores, only make the wait stricter).
+        // stores, only make the wait stricter). The barrier also drains the
+        // previous tile's stores: left outstanding, they make the compiler
+        // guard the k loop's fragment reads with a full vmcnt(0) every step.
         wait_vmcnt_stages<LOADS, NS - 2>(min(NS - 2, nk - 1));
         __syncthreads();
         if (wave_active) read_frags(0, 0, 0);
@@ -447,51 +460,61 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         // lane swap), so that the even lane holds columns (c, c+1) of row R
         // and the odd lane the same columns of row R+1. Each store instruction
         // then writes four whole 64-byte (bf16) or 128-byte (fp32) row
-        // segments.
+        // segments. A full tile stores without per-element checks.
         const bool even = (lane & 1) == 0;
         const int cpair = (lane & 31) & ~1;
-        if (GATEUP) {
-            uint16_t *H = (uint16_t *)a.C;
-            const int fN = N / 2;
+        const bool full = cur.rows == BM && cur.n0 + BN <= N;
+        auto epilogue = [&](auto checked_t) {
+            constexpr bool checked = decltype(checked_t)::value;
+            if constexpr (GATEUP) {
+                uint16_t *H = (uint16_t *)a.C;
+                const int fN = N / 2;
+                const int fc0 = ((cur.n0 + wn * TN) / 64) * 32 + cpair;   // first H column pair
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
+                for (int i = 0; i < MI; ++i) {
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const int m = wm * TM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3) + (even ? 0 : 1);
-                    uint16_t *hrow = H + (int64_t)(cur.row0 + min(m, cur.rows - 1)) * a.ldc;
+                    for (int r = 0; r < 16; r += 2) {
+                        const int m = wm * TM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3) + (even ? 0 : 1);
+                        uint16_t *hrow = H + (int64_t)(cur.row0 + (checked ? min(m, cur.rows - 1) : m)) * a.ldc + fc0;
 #pragma unroll
-                    for (int q = 0; q < NI / 2; ++q) {
-                        const uint32_t h0 = f32_to_bf16(silu_mul_fast(acc[i][2 * q][r], acc[i][2 * q + 1][r]));
-                        const uint32_t h1 =
-                            f32_to_bf16(silu_mul_fast(acc[i][2 * q][r + 1], acc[i][2 * q + 1][r + 1]));
-                        const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)(even ? h1 : h0), 0xB1, 0xF, 0xF, false);
-                        const uint32_t packed = even ? (h0 | (y << 16)) : (y | (h1 << 16));
-                        const int fcol = ((cur.n0 + wn * TN) / 64 + q) * 32 + cpair;
-                        if (m < cur.rows && fcol < fN) *(uint32_t *)(hrow + fcol) = packed;
+                        for (int q = 0; q < NI / 2; ++q) {
+                            const float s0 = silu_mul_fast(acc[i][2 * q][r], acc[i][2 * q + 1][r]);
+                            const float s1 = silu_mul_fast(acc[i][2 * q][r + 1], acc[i][2 * q + 1][r + 1]);
+                            const float y = __int_as_float(
+                                __builtin_amdgcn_mov_dpp(__float_as_int(even ? s1 : s0), 0xB1, 0xF, 0xF, false));
+                            const uint32_t packed = even ? pack_bf16x2(s0, y) : pack_bf16x2(y, s1);
+                            if (!checked || (m < cur.rows && fc0 + q * 32 < fN)) *(uint32_t *)(hrow + q * 32) = packed;
+                        }
+                    }
+                }
+            } else {
+                float *Yr = (float *)a.C + cur.ks * a.split_stride;
+                const int n0w = cur.n0 + wn * TN + cpair;
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        const int m = wm * TM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3) + (even ? 0 : 1);
+                        const int mc = checked ? min(m, cur.rows - 1) : m;
+                        float *yrow = Yr + (int64_t)s_route[par][mc] * a.ldc + n0w;
+                        const float al = s_alpha[par][mc];
+#pragma unroll
+                        for (int j = 0; j < NI; ++j) {
+                            const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+                            const float y = __int_as_float(
+                                __builtin_amdgcn_mov_dpp(__float_as_int(even ? v1 : v0), 0xB1, 0xF, 0xF, false));
+                            const float2 o = even ? make_float2(al * v0, al * y) : make_float2(al * y, al * v1);
+                            if (!checked || (m < cur.rows && n0w + j * 32 < N)) *(float2 *)(yrow + j * 32) = o;
+                        }
                     }
                 }
             }
-        } else {
-            float *Yr = (float *)a.C + cur.ks * a.split_stride;
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const int m = wm * TM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3) + (even ? 0 : 1);
-                    const int mc = min(m, cur.rows - 1);
-                    float *yrow = Yr + (int64_t)s_route[par][mc] * a.ldc;
-                    const float al = s_alpha[par][mc];
-#pragma unroll
-                    for (int j = 0; j < NI; ++j) {
-                        const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
-                        const float y = __int_as_float(
-                            __builtin_amdgcn_mov_dpp(__float_as_int(even ? v1 : v0), 0xB1, 0xF, 0xF, false));
-                        const float2 o = even ? make_float2(al * v0, al * y) : make_float2(al * y, al * v1);
-                        const int n = cur.n0 + wn * TN + j * 32 + cpair;
-                        if (m < cur.rows && n < N) *(float2 *)(yrow + n) = o;
-                    }
-                }
-            }
+        };
+        if (full)
+            epilogue(std::integral_constant<bool, false>());
+        else
+            epilogue(std::integral_constant<bool, true>());
+        if constexpr (!GATEUP) {
             if (cur.n0 == 0 && cur.ks == 0)
                 for (int m = tid; m < cur.rows; m += NT) a.done[s_route[par][m]] = 1;
         }
