@@ -455,12 +455,12 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         }
 
         // Result layout: register r of lane l holds row 8*(r/4) + 4*(l/32) +
-        // r%4 and column l%32 of its 32x32 block. Registers r and r+1 (r even)
-        // are rows R and R+1; adjacent lanes swap one of the two values (a DPP
-        // lane swap), so that the even lane holds columns (c, c+1) of row R
-        // and the odd lane the same columns of row R+1. Each store instruction
-        // then writes four whole 64-byte (bf16) or 128-byte (fp32) row
-        // segments. A full tile stores without per-element checks.
+        // r%4 and column l%32 of its 32x32 block. Gate/up: registers r and r+1
+        // (r even) are rows R and R+1; adjacent lanes swap one of the two
+        // values (a DPP lane swap), so that the even lane holds columns
+        // (c, c+1) of row R and the odd lane the same columns of row R+1, and
+        // each store instruction writes four whole 64-byte row segments of H.
+        // A full tile stores without per-element checks.
         const bool even = (lane & 1) == 0;
         const int cpair = (lane & 31) & ~1;
         const bool full = cur.rows == BM && cur.n0 + BN <= N;
@@ -488,24 +488,23 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                     }
                 }
             } else {
+                // Down: each accumulator register is stored as it stands, lanes
+                // 0-31 writing 32 consecutive columns (128 bytes) of row R and
+                // lanes 32-63 the same columns of row R+4: plain 4-byte stores
+                // drain faster per CU than paired 8-byte ones and need no swap.
                 float *Yr = (float *)a.C + cur.ks * a.split_stride;
-                const int n0w = cur.n0 + wn * TN + cpair;
+                const int ncol = cur.n0 + wn * TN + (lane & 31);
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
 #pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        const int m = wm * TM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3) + (even ? 0 : 1);
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = wm * TM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
                         const int mc = checked ? min(m, cur.rows - 1) : m;
-                        float *yrow = Yr + (int64_t)s_route[par][mc] * a.ldc + n0w;
+                        float *yrow = Yr + (int64_t)s_route[par][mc] * a.ldc + ncol;
                         const float al = s_alpha[par][mc];
 #pragma unroll
-                        for (int j = 0; j < NI; ++j) {
-                            const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
-                            const float y = __int_as_float(
-                                __builtin_amdgcn_mov_dpp(__float_as_int(even ? v1 : v0), 0xB1, 0xF, 0xF, false));
-                            const float2 o = even ? make_float2(al * v0, al * y) : make_float2(al * y, al * v1);
-                            if (!checked || (m < cur.rows && n0w + j * 32 < N)) *(float2 *)(yrow + j * 32) = o;
-                        }
+                        for (int j = 0; j < NI; ++j)
+                            if (!checked || (m < cur.rows && ncol + j * 32 < N)) yrow[j * 32] = al * acc[i][j][r];
                     }
                 }
             }
