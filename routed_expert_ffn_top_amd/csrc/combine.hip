@@ -14,6 +14,10 @@
 namespace moe {
 namespace {
 
+// KP > 0: the token has exactly KP routes and the down projection does not
+// split its K; every route row is requested before the first add, so a
+// thread has KP loads in flight. KP == 0: any kp and split count.
+template <int KP>
 __global__ __launch_bounds__(256) void k_combine(float *__restrict__ Y, int64_t ldy,
                                                  const float *__restrict__ Yr,
                                                  const int32_t *__restrict__ done, int d, int kp,
@@ -23,15 +27,34 @@ __global__ __launch_bounds__(256) void k_combine(float *__restrict__ Y, int64_t 
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= d) return;
     float4 y = *(const float4 *)(Y + (int64_t)t * ldy + c);
-    for (int j = 0; j < kp; ++j) {
-        const int64_t i = (int64_t)t * kp + j;
-        if (done[i]) {
-            for (int q = 0; q < splits; ++q) {   // route j's partial rows, in order
-                const float4 v = *(const float4 *)(Yr + q * split_stride + i * d + c);
-                y.x += v.x;
-                y.y += v.y;
-                y.z += v.z;
-                y.w += v.w;
+    if constexpr (KP > 0) {
+        bool ok[KP];
+        float4 v[KP];
+#pragma unroll
+        for (int j = 0; j < KP; ++j) ok[j] = done[(int64_t)t * KP + j] != 0;
+#pragma unroll
+        for (int j = 0; j < KP; ++j)
+            v[j] = ok[j] ? *(const float4 *)(Yr + ((int64_t)t * KP + j) * d + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int j = 0; j < KP; ++j) {   // ascending j; a route left out adds nothing
+            if (ok[j]) {
+                y.x += v[j].x;
+                y.y += v[j].y;
+                y.z += v[j].z;
+                y.w += v[j].w;
+            }
+        }
+    } else {
+        for (int j = 0; j < kp; ++j) {
+            const int64_t i = (int64_t)t * kp + j;
+            if (done[i]) {
+                for (int q = 0; q < splits; ++q) {   // route j's partial rows, in order
+                    const float4 v = *(const float4 *)(Yr + q * split_stride + i * d + c);
+                    y.x += v.x;
+                    y.y += v.y;
+                    y.z += v.z;
+                    y.w += v.w;
+                }
             }
         }
     }
@@ -92,8 +115,19 @@ hipError_t launch_combine(const moe_shape &s, float *Y, const float *Yr, const i
 {
     if (s.T == 0) return hipSuccess;
     const dim3 grid((unsigned)((s.d / 4 + 255) / 256), (unsigned)s.T);
-    hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, st, Y, s.ldy, Yr, done, s.d,
-                       s.k + s.n_shared, down_splits(s), (int64_t)s.T * (s.k + s.n_shared) * s.d);
+    const int kp = s.k + s.n_shared, splits = down_splits(s);
+    const int64_t sstride = (int64_t)s.T * kp * s.d;
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, Y, s.ldy, Yr, done, s.d, kp, splits, sstride);
+    };
+    if (splits == 1 && kp == 8)
+        go(k_combine<8>);
+    else if (splits == 1 && kp == 2)
+        go(k_combine<2>);
+    else if (splits == 1 && kp == 6)
+        go(k_combine<6>);
+    else
+        go(k_combine<0>);
     return hipGetLastError();
 }
 
