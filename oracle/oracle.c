@@ -24,7 +24,13 @@
  *                         cursor pass in ascending route index storing (t_i, i).
  *   oracle_expert_ffn     Eq. (2) Y_t = A_t + sum alpha F_e(X_t) with Eq. (1)
  *                         F_e(x) = W_d (SiLU(W_g x) * (W_u x)), per token and
- *                         per selected expert, accumulated in fp64.
+ *                         per selected expert, accumulated in fp64. With row
+ *                         scales, each weight is its stored value times its
+ *                         row's scale (weight-only quantised experts).
+ *   oracle_fp8e4m3_decode the value of an fp8 e4m3 code (OCP 8-bit floating
+ *                         point: sign, 4 exponent bits with bias 7, 3 mantissa
+ *                         bits; exponent 0 is subnormal; S.1111.111 is NaN;
+ *                         there are no infinities).
  *
  * Parity status: every function is pinned by CPU tests (brute force, closed
  * forms, special cases and invariants); none is "parity unpinned".
@@ -190,6 +196,28 @@ int64_t oracle_route_map(int64_t kp, int64_t t0, int64_t nt, const int32_t *idx,
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /*
+ * fp8 e4m3 codes to fp32 values (exact: every code's value has at most 4
+ * significant bits and an exponent in [-9, 8]).
+ *   code = s eeee mmm:  e = 0:        (-1)^s * m/8 * 2^-6
+ *                       e = 15, m = 7: NaN
+ *                       otherwise:    (-1)^s * (1 + m/8) * 2^(e-7)
+ */
+void oracle_fp8e4m3_decode(int64_t n, const uint8_t *q, float *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const int sgn = q[i] >> 7, e = (q[i] >> 3) & 15, m = q[i] & 7;
+        double v;
+        if (e == 15 && m == 7)
+            v = NAN;
+        else if (e == 0)
+            v = ldexp((double)m / 8.0, -6);
+        else
+            v = ldexp(1.0 + (double)m / 8.0, e - 7);
+        out[i] = (float)(sgn ? -v : v);
+    }
+}
+
+/*
  * Expert FFN and weighted combine for the listed tokens, Eq. (1)-(2):
  *   y = A[t]; for j = 0 .. kp-1 (routes of token t whose mask byte is nonzero,
  *   all of them when route_mask is NULL), with e = idx[t][j]:
@@ -200,12 +228,16 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
  * in fp64.  X: [T][ldx] fp32 values; Wg, Wu: [n_exp][f][d]; Wd: [n_exp][d][f];
  * A: [T][d] fp32 or NULL (zero residual); Y: [n_tok][d] fp64, row r for token
  * tokens[r].  route_mask is indexed by the global route id t*kp + j.
+ * Sg, Su: [n_exp][f] and Sd: [n_exp][d] row scales, or all NULL: weight
+ * Wg[e][n][i] stands for Wg[e][n][i] * Sg[e][n] (likewise Wu, and Wd with
+ * Sd[e][m]), the product taken in fp64.
  */
 void oracle_expert_ffn(int64_t d, int64_t f, int64_t kp, int64_t n_tok,
                        const int64_t *tokens, const float *X, int64_t ldx,
                        const int32_t *idx, const double *alpha,
                        const unsigned char *route_mask, const float *Wg,
-                       const float *Wu, const float *Wd, const float *A,
+                       const float *Wu, const float *Wd, const float *Sg,
+                       const float *Su, const float *Sd, const float *A,
                        double *Y)
 {
     int64_t r;
@@ -226,18 +258,21 @@ void oracle_expert_ffn(int64_t d, int64_t f, int64_t kp, int64_t n_tok,
             const float *wu = Wu + e * f * d;
             const float *wd = Wd + e * d * f;
             for (int64_t n = 0; n < f; ++n) {
+                const double scg = Sg ? (double)Sg[e * f + n] : 1.0;
+                const double scu = Su ? (double)Su[e * f + n] : 1.0;
                 double sg = 0.0, su = 0.0;
                 for (int64_t c = 0; c < d; ++c) {
-                    sg += (double)wg[n * d + c] * (double)x[c];
-                    su += (double)wu[n * d + c] * (double)x[c];
+                    sg += (double)wg[n * d + c] * scg * (double)x[c];
+                    su += (double)wu[n * d + c] * scu * (double)x[c];
                 }
                 g[n] = sg;
                 u[n] = su;
             }
             for (int64_t n = 0; n < f; ++n) h[n] = silu(g[n]) * u[n];
             for (int64_t m = 0; m < d; ++m) {
+                const double scd = Sd ? (double)Sd[e * d + m] : 1.0;
                 double o = 0.0;
-                for (int64_t n = 0; n < f; ++n) o += (double)wd[m * f + n] * h[n];
+                for (int64_t n = 0; n < f; ++n) o += (double)wd[m * f + n] * scd * h[n];
                 y[m] += alpha[i] * o;
             }
         }

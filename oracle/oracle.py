@@ -60,8 +60,11 @@ class Oracle:
                                          _ptr, _ptr, _ptr, _ptr, _ptr]
         lib.oracle_route_map.restype = _i64
         lib.oracle_expert_ffn.argtypes = [_i64, _i64, _i64, _i64, _ptr, _ptr, _i64, _ptr,
-                                          _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr]
+                                          _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr,
+                                          _ptr, _ptr]
         lib.oracle_expert_ffn.restype = None
+        lib.oracle_fp8e4m3_decode.argtypes = [_i64, _ptr, _ptr]
+        lib.oracle_fp8e4m3_decode.restype = None
         lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -117,10 +120,20 @@ class Oracle:
                     rec_route=rec_route[:n_valid], route_pos=route_pos,
                     n_valid=int(n_valid))
 
+    def fp8e4m3_decode(self, q: np.ndarray) -> np.ndarray:
+        """Values (fp32) of fp8 e4m3 codes (uint8 array of any shape)."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        out = np.empty(q.shape, dtype=np.float32)
+        self.lib.oracle_fp8e4m3_decode(q.size, _p(q), _p(out))
+        return out
+
     def expert_ffn(self, X: np.ndarray, idx: np.ndarray, alpha: np.ndarray,
                    Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
                    A: Optional[np.ndarray] = None, tokens=None,
-                   route_mask: Optional[np.ndarray] = None) -> np.ndarray:
+                   route_mask: Optional[np.ndarray] = None,
+                   scales: Optional[tuple] = None) -> np.ndarray:
+        """scales: None, or (Sg [ne][f], Su [ne][f], Sd [ne][d]) row scales;
+        each weight is then its given value times its row's scale."""
         X = np.ascontiguousarray(X, dtype=np.float32)
         T, d = X.shape
         ne, f, d2 = Wg.shape
@@ -139,14 +152,19 @@ class Oracle:
         if route_mask is not None:
             mask = np.ascontiguousarray(route_mask, dtype=np.uint8).reshape(-1)
             assert mask.size == T * kp
+        Sg = Su = Sd = None
+        if scales is not None:
+            Sg, Su, Sd = (np.ascontiguousarray(v, dtype=np.float32) for v in scales)
+            assert Sg.shape == (ne, f) and Su.shape == (ne, f) and Sd.shape == (ne, d)
         Y = np.empty((len(tokens), d), dtype=np.float64)
         self.lib.oracle_expert_ffn(d, f, kp, len(tokens), _p(tokens), _p(X), d, _p(idx),
-                                   _p(alpha), _p(mask), _p(Wg), _p(Wu), _p(Wd), _p(A), _p(Y))
+                                   _p(alpha), _p(mask), _p(Wg), _p(Wu), _p(Wd), _p(Sg), _p(Su),
+                                   _p(Sd), _p(A), _p(Y))
         return Y
 
     # -- whole layer -------------------------------------------------------
     def layer(self, X, Wr, bias, Wg, Wu, Wd, A, k, n_shared, renorm,
-              phi=None, P=None, tokens=None, logits=None):
+              phi=None, P=None, tokens=None, logits=None, scales=None):
         """Router (unless logits are given) -> top-k -> route map -> FFN."""
         L = self.router_logits(X, Wr, bias) if logits is None else logits
         idx, alpha = self.topk(L, k, n_shared, renorm)
@@ -155,7 +173,7 @@ class Oracle:
             phi = np.arange(ne, dtype=np.int32)
             P = ne
         rm = self.route_map(idx, phi, P)
-        Y = self.expert_ffn(X, idx, alpha, Wg, Wu, Wd, A, tokens=tokens)
+        Y = self.expert_ffn(X, idx, alpha, Wg, Wu, Wd, A, tokens=tokens, scales=scales)
         return dict(logits=L, idx=idx, alpha=alpha, Y=Y, **rm)
 
 

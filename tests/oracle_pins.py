@@ -366,6 +366,51 @@ def check_ffn_special(orc):
     assert _rel(Yf, Y) < 1e-13
 
 
+# ------------------------------------------ fp8 weights (weight-only) --
+def check_fp8_decode(orc):
+    """Every e4m3 code against PyTorch's own float8_e4m3fn conversion (an
+    independent implementation of the same OCP format), plus closed-form
+    anchors of the format."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.fp8e4m3_decode(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    anchors = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+               0x3C: 1.5, 0x7E: 448.0, 0xFE: -448.0, 0xB8: -1.0}
+    for c, v in anchors.items():
+        assert got[c] == v, (hex(c), got[c], v)
+    assert np.signbit(got[0x80]) and got[0x80] == 0.0 and not np.signbit(got[0x00])
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert np.all(np.diff(got[:0x7F].astype(np.float64)) > 0)          # positive codes ascend
+    assert np.array_equal(got[0x80:0xFF], -got[:0x7F])                  # sign bit negates
+
+
+def check_ffn_row_scales(orc):
+    """Weights given as fp8 code values with per-row scales equal the dense
+    fp64 brute force on value * scale; unit scales change nothing."""
+    rng = _rng(43)
+    T, d, f, E, k = 12, 64, 96, 5, 2
+    X = _bf16_values(rng.standard_normal((T, d), dtype=np.float32))
+    A = rng.standard_normal((T, d), dtype=np.float32)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    qg, qu = (orc.fp8e4m3_decode(rng.choice(finite, size=(E, f, d))) for _ in range(2))
+    qd = orc.fp8e4m3_decode(rng.choice(finite, size=(E, d, f)))
+    Sg, Su = (np.exp(rng.uniform(-9, -5, size=(E, f))).astype(np.float32) for _ in range(2))
+    Sd = np.exp(rng.uniform(-9, -5, size=(E, d))).astype(np.float32)
+    idx, alpha = _random_routes(rng, T, E, k)
+    Y = orc.expert_ffn(X, idx, alpha, qg, qu, qd, A, scales=(Sg, Su, Sd))
+    ref = dense_brute_force(X, idx, alpha, qg.astype(np.float64) * Sg[:, :, None].astype(np.float64),
+                            qu.astype(np.float64) * Su[:, :, None].astype(np.float64),
+                            qd.astype(np.float64) * Sd[:, :, None].astype(np.float64), A)
+    assert _rel(Y, ref) < 1e-12, _rel(Y, ref)
+    ones = (np.ones((E, f), np.float32), np.ones((E, f), np.float32), np.ones((E, d), np.float32))
+    assert np.array_equal(orc.expert_ffn(X, idx, alpha, qg, qu, qd, A, scales=ones),
+                          orc.expert_ffn(X, idx, alpha, qg, qu, qd, A))
+
+
 def check_layer_chain(orc):
     """The whole chain on a tiny layer equals the brute-force chain."""
     rng = _rng(51)
@@ -390,4 +435,5 @@ ALL_CHECKS = [check_router_golden, check_router_exact_integers, check_router_err
               check_topk_bruteforce, check_topk_special, check_topk_nan_and_signed_zero, check_alpha,
               check_shared,
               check_route_map_golden, check_route_map_bruteforce, check_route_map_errors,
-              check_ffn_dense_bruteforce, check_ffn_special, check_layer_chain]
+              check_ffn_dense_bruteforce, check_ffn_special, check_fp8_decode, check_ffn_row_scales,
+              check_layer_chain]

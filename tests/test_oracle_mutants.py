@@ -49,6 +49,13 @@ MUTANTS = [
      "for (int64_t j = 0; j < kp - 1; ++j) {\n            const int64_t i = t * kp + j;"),
     ("route mask ignored", "if (route_mask && !route_mask[i]) continue;", ""),
     ("up projection reads the gate weights", "su += (double)wu[n * d + c]", "su += (double)wg[n * d + c]"),
+    ("fp8 exponent bias off by one", "v = ldexp(1.0 + (double)m / 8.0, e - 7);",
+     "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("fp8 subnormals one binade low", "v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
+    ("fp8 sign ignored", "out[i] = (float)(sgn ? -v : v);", "out[i] = (float)v;"),
+    ("up projection takes the gate scales", "const double scu = Su ? (double)Su[e * f + n] : 1.0;",
+     "const double scu = Sg ? (double)Sg[e * f + n] : 1.0;"),
+    ("down row scale not applied", "(double)wd[m * f + n] * scd * h[n]", "(double)wd[m * f + n] * h[n]"),
 ]
 
 
