@@ -55,6 +55,15 @@ typedef void *moe_stream; /* a hipStream_t */
 
 #define MOE_DT_F32 0
 #define MOE_DT_BF16 1
+/* bf16 activations; expert weights stored as fp8 e4m3 codes (OCP 8-bit
+ * float: sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+ * S.1111.111 is NaN) with one fp32 scale per weight row, a weight being code
+ * times its row's scale: the weight-only quantised experts of the pages'
+ * quantised-weight path. Each slice ([2f][d] packed gate/up, or [d][f] down)
+ * stores its codes row-major followed by its rows' fp32 scales ([2f] or
+ * [d]); slot strides are then in bytes. The expert kernels decode the codes
+ * to bf16 operands exactly and scale the fp32 accumulators. */
+#define MOE_DT_BF16_FP8W 2
 
 /* Device error word bits (moe_device_errors). */
 #define MOE_DEVERR_EXPERT_ID 1 /* a top-k id outside [0, E + n_shared) */
@@ -86,7 +95,8 @@ typedef void *moe_stream; /* a hipStream_t */
  * across invocations by token range).
  * Limits: 1 <= k <= E <= 256, k + n_shared <= 64, E + n_shared <= 512,
  * 1 <= P <= 512, T >= 0.
- * bf16: d % 64 == 0, f % 64 == 0. fp32: d % 4 == 0, f % 32 == 0.
+ * bf16 and bf16 with fp8 weights: d % 64 == 0, f % 64 == 0.
+ * fp32: d % 4 == 0, f % 32 == 0.
  */
 typedef struct moe_shape {
     int32_t T;
@@ -97,7 +107,7 @@ typedef struct moe_shape {
     int32_t n_shared;
     int32_t P;
     int32_t capacity; /* C, >= 1 */
-    int32_t dtype;    /* MOE_DT_BF16 or MOE_DT_F32 */
+    int32_t dtype;    /* MOE_DT_BF16, MOE_DT_BF16_FP8W or MOE_DT_F32 */
     int32_t renorm;   /* 1: top-k weights renormalised over the k selected */
     int64_t ldx;      /* row stride of X in elements, >= d */
     int64_t ldy;      /* row stride of Y in elements, >= d, multiple of 4 */
@@ -269,7 +279,9 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X,
  * 64q+32..64q+63 are up rows 32q..32q+31. The down slice is W_d [d][f]
  * unchanged.
  * moe_pack_gate_up: device, n experts, source expert stride src_stride and
- * destination stride dst_stride (elements).
+ * destination stride dst_stride (elements; bytes for MOE_DT_BF16_FP8W, whose
+ * W_g and W_u slices are [f][d] codes followed by [f] row scales each, and
+ * whose packed slice gets its 2f row scales in the packed row order).
  * moe_pack_gate_up_host: the same on host memory, synchronous.
  */
 moe_status moe_pack_gate_up(const moe_shape *shape, const void *W_g,
@@ -283,6 +295,8 @@ moe_status moe_pack_gate_up_host(const moe_shape *shape, const void *W_g,
  * Slot arena (Eq. 3: the slice j of slot s starts at plane_j + s * S_j).
  *   plane_gu  device, P slots of [2f][d] dtype, slot stride stride_gu
  *   plane_d   device, P slots of [d][f] dtype, slot stride stride_d
+ *   (MOE_DT_BF16_FP8W: each slice is its codes then its row scales, and the
+ *   strides are in bytes: stride_gu >= 2f*d + 8f, stride_d >= d*f + 4d)
  *   G         slots per bank (1 <= G <= P, P % G == 0); banks are used when
  *             paging (Eq. 4: phi(e) = b*G + r(e))
  * Creates the residency table with every slot Available.

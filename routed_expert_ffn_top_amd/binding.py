@@ -25,6 +25,9 @@ MOE_ERR_HIP = -5
 MOE_ERR_UNSUPPORTED = -6
 MOE_DT_F32 = 0
 MOE_DT_BF16 = 1
+MOE_DT_BF16_FP8W = 2   # bf16 activations, fp8 e4m3 weights with fp32 row scales
+_DTYPE_CODE = {"f32": MOE_DT_F32, "bf16": MOE_DT_BF16, "bf16_fp8w": MOE_DT_BF16_FP8W,
+               MOE_DT_F32: MOE_DT_F32, MOE_DT_BF16: MOE_DT_BF16, MOE_DT_BF16_FP8W: MOE_DT_BF16_FP8W}
 MOE_DEVERR_EXPERT_ID = 1
 MOE_ROUTE_RESET = 1
 MOE_FFN_EXPERTS = 1
@@ -137,7 +140,7 @@ def make_shape(T, d, f, E, k, n_shared=0, P=None, capacity=None, dtype="bf16", r
     return moe_shape(T=T, d=d, f=f, E=E, k=k, n_shared=n_shared,
                      P=(E + n_shared) if P is None else P,
                      capacity=max(1, T * kp) if capacity is None else capacity,
-                     dtype=MOE_DT_BF16 if dtype in ("bf16", MOE_DT_BF16) else MOE_DT_F32,
+                     dtype=_DTYPE_CODE[dtype],
                      renorm=int(bool(renorm)), ldx=d if ldx is None else ldx,
                      ldy=d if ldy is None else ldy)
 
@@ -294,11 +297,18 @@ class Arena:
 
     def __init__(self, shape: moe_shape, G: Optional[int] = None, device="cuda"):
         self.shape = shape
-        dt = torch.bfloat16 if shape.dtype == MOE_DT_BF16 else torch.float32
-        self.stride_gu = 2 * shape.f * shape.d
-        self.stride_d = shape.d * shape.f
-        self.plane_gu = torch.empty((shape.P, 2 * shape.f, shape.d), dtype=dt, device=device)
-        self.plane_d = torch.empty((shape.P, shape.d, shape.f), dtype=dt, device=device)
+        if shape.dtype == MOE_DT_BF16_FP8W:
+            # a slice is its codes then its row scales; strides in bytes
+            self.stride_gu = 2 * shape.f * shape.d + 8 * shape.f
+            self.stride_d = shape.d * shape.f + 4 * shape.d
+            self.plane_gu = torch.empty((shape.P, self.stride_gu), dtype=torch.uint8, device=device)
+            self.plane_d = torch.empty((shape.P, self.stride_d), dtype=torch.uint8, device=device)
+        else:
+            dt = torch.bfloat16 if shape.dtype == MOE_DT_BF16 else torch.float32
+            self.stride_gu = 2 * shape.f * shape.d
+            self.stride_d = shape.d * shape.f
+            self.plane_gu = torch.empty((shape.P, 2 * shape.f, shape.d), dtype=dt, device=device)
+            self.plane_d = torch.empty((shape.P, shape.d, shape.f), dtype=dt, device=device)
         self.G = shape.P if G is None else G
         self.handle = moe_arena_create(shape, self.plane_gu, self.plane_d, self.stride_gu,
                                        self.stride_d, self.G)
@@ -314,14 +324,26 @@ class Arena:
         except Exception:
             pass
 
-    def load_resident(self, Wg, Wu, Wd, phi: Sequence[int], stream=None):
-        """Pack and publish every expert e with phi[e] >= 0 into slot phi[e]."""
+    def load_resident(self, Wg, Wu, Wd, phi: Sequence[int], stream=None, scales=None):
+        """Pack and publish every expert e with phi[e] >= 0 into slot phi[e].
+        scales: (Sg, Su, Sd) row scales when the weights are fp8 codes."""
         for e, s in enumerate(phi):
             if s < 0:
                 continue
-            moe_pack_gate_up(self.shape, Wg[e], Wu[e], self.plane_gu[s], 1, 0, 0, stream)
-            self.plane_d[s].copy_(Wd[e])
+            g, u, dn = expert_slices(Wg, Wu, Wd, scales, e)
+            moe_pack_gate_up(self.shape, g, u, self.plane_gu[s], 1, 0, 0, stream)
+            self.plane_d[s].copy_(dn.reshape(self.plane_d[s].shape))
             arena_publish_slot(self, s, e, stream)
+
+
+def expert_slices(Wg, Wu, Wd, scales, e):
+    """Expert e's gate, up and down slices in the layout the C ABI takes:
+    the weight rows, then (fp8 codes) the rows' fp32 scales as bytes."""
+    if scales is None:
+        return Wg[e], Wu[e], Wd[e]
+    Sg, Su, Sd = scales
+    cat = lambda q, sc: torch.cat([q[e].reshape(-1), sc[e].contiguous().view(torch.uint8)])
+    return cat(Wg, Sg), cat(Wu, Su), cat(Wd, Sd)
 
 
 def moe_profile_begin(kernel: str, max_launches: int):

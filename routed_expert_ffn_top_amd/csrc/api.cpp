@@ -72,12 +72,12 @@ moe_status check_shape(const moe_shape *s)
     if (s->k + s->n_shared > 64) return fail(MOE_ERR_UNSUPPORTED, "k + n_shared must be <= 64");
     if (s->P < 1 || s->P > kMaxExp) return fail(MOE_ERR_INVALID_ARG, "need 1 <= P <= %d", kMaxExp);
     if (s->capacity < 1) return fail(MOE_ERR_INVALID_ARG, "capacity must be >= 1");
-    if (s->dtype != MOE_DT_BF16 && s->dtype != MOE_DT_F32)
-        return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_DT_BF16 or MOE_DT_F32");
+    if (s->dtype != MOE_DT_BF16 && s->dtype != MOE_DT_F32 && s->dtype != MOE_DT_BF16_FP8W)
+        return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_DT_BF16, MOE_DT_BF16_FP8W or MOE_DT_F32");
     if (s->ldx < s->d || s->ldy < s->d || (s->ldy % 4) != 0)
         return fail(MOE_ERR_INVALID_ARG, "need ldx >= d, ldy >= d, ldy %% 4 == 0");
     if ((s->d % 4) != 0) return fail(MOE_ERR_UNSUPPORTED, "d must be a multiple of 4");
-    if (s->dtype == MOE_DT_BF16) {
+    if (act_bf16(*s)) {
         if ((s->d % 64) != 0 || (s->f % 64) != 0)
             return fail(MOE_ERR_UNSUPPORTED, "bf16 layers need d %% 64 == 0 and f %% 64 == 0");
         if ((s->ldx % 8) != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 X needs ldx %% 8 == 0");
@@ -184,7 +184,7 @@ struct moe_arena {
     moe_shape shape;
     char *plane_gu;
     char *plane_d;
-    int64_t stride_gu, stride_d;  // elements
+    int64_t stride_gu, stride_d;  // elements (bytes for fp8 weights)
     int G;
     int esz;
     std::vector<int> state, owner, slot_of;  // per slot, per slot, per expert
@@ -252,7 +252,10 @@ moe_status arena_bind_many_locked(moe_arena *a, const int *sl, const int *ex, in
                                   const void *const *src_d, hipStream_t st, bool timed)
 {
     const moe_shape &s = a->shape;
-    const size_t gu_bytes = (size_t)2 * s.f * s.d * a->esz, d_bytes = (size_t)s.d * s.f * a->esz;
+    const size_t gu_bytes = gu_slice_bytes(s), d_bytes = d_slice_bytes(s);
+    // one transfer may cover several slots only where the plane holds the
+    // slices back to back
+    const bool packed_planes = (size_t)a->stride_gu * a->esz == gu_bytes && (size_t)a->stride_d * a->esz == d_bytes;
     for (int i = 0; i < n; ++i)
         if (!src_gu[i] || !src_d[i]) return fail(MOE_ERR_INVALID_ARG, "bind source is NULL");
     int reserved = 0;
@@ -270,7 +273,7 @@ moe_status arena_bind_many_locked(moe_arena *a, const int *sl, const int *ex, in
     const int pi = (rc == MOE_OK && e == hipSuccess && timed) ? prof_begin(MOE_KERNEL_H2D, st) : -1;
     for (int i = 0; i < n && rc == MOE_OK && e == hipSuccess;) {
         int j = i + 1;   // extend while slots are consecutive and host slices contiguous
-        while (j < n && sl[j] == sl[j - 1] + 1 &&
+        while (packed_planes && j < n && sl[j] == sl[j - 1] + 1 &&
                (const char *)src_gu[j] == (const char *)src_gu[j - 1] + gu_bytes &&
                (const char *)src_d[j] == (const char *)src_d[j - 1] + d_bytes)
             ++j;
@@ -387,11 +390,15 @@ GemmArgs gemm_args(const moe_shape &s, const moe_routes &r, const moe_arena *a)
 moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, const moe_routes &r,
                         moe_arena *a, int max_rows, bool simple, void *ws, hipStream_t st)
 {
+    if (simple && w_fp8(s))
+        return fail(MOE_ERR_UNSUPPORTED, "the plain kernel reads bf16 or fp32 weights only");
     GemmArgs g = gemm_args(s, r, a);
     g.A = X;
     g.lda = s.ldx;
     g.B = a->plane_gu;
     g.slot_stride = a->stride_gu;
+    g.bfp8 = w_fp8(s);
+    g.scale_off = (int64_t)2 * s.f * s.d;   // fp8: the row scales follow the codes
     g.N = 2 * s.f;
     g.K = s.d;
     g.C = ws_at<char>(ws, w.H);
@@ -402,6 +409,8 @@ moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, co
     h.lda = s.f;
     h.B = a->plane_d;
     h.slot_stride = a->stride_d;
+    h.bfp8 = w_fp8(s);
+    h.scale_off = (int64_t)s.d * s.f;
     h.N = s.d;
     h.K = s.f;
     h.C = ws_at<float>(ws, w.Yr);
@@ -506,7 +515,7 @@ moe_status moe_expert_ffn(const moe_shape *shape, const void *X, float *Y, const
             arena->shape.dtype != shape->dtype || arena->shape.E != shape->E ||
             arena->shape.n_shared != shape->n_shared)
             return fail(MOE_ERR_INVALID_ARG, "arena was made for another shape");
-        if (shape->dtype == MOE_DT_BF16 && !aligned(X, 16))
+        if (act_bf16(*shape) && !aligned(X, 16))
             return fail(MOE_ERR_INVALID_ARG, "X must be 16-byte aligned");
         PhiArg pa;
         MOE_TRY(check_phi(shape, phi, &pa));
@@ -531,9 +540,12 @@ moe_status moe_pack_gate_up(const moe_shape *shape, const void *W_g, const void 
 {
     MOE_TRY(check_shape(shape));
     if (!W_g || !W_u || !dst || n < 0) return fail(MOE_ERR_INVALID_ARG, "pack: bad arguments");
-    const int64_t fd = (int64_t)shape->f * shape->d;
-    if (n > 1 && (src_stride < fd || dst_stride < 2 * fd))
+    const int esz = w_esz(*shape);
+    const size_t src_bytes = (size_t)shape->f * shape->d * esz + (w_fp8(*shape) ? (size_t)shape->f * 4 : 0);
+    if (n > 1 && ((size_t)src_stride * esz < src_bytes || (size_t)dst_stride * esz < gu_slice_bytes(*shape)))
         return fail(MOE_ERR_INVALID_ARG, "pack: strides smaller than a slice");
+    if (((src_stride * esz) % 4) != 0 || ((dst_stride * esz) % 4) != 0)
+        return fail(MOE_ERR_INVALID_ARG, "pack: strides must be whole 32-bit words");
     HIP_TRY(launch_pack_gate_up(*shape, W_g, W_u, dst, n, src_stride, dst_stride, S(stream)), "pack launch");
     return MOE_OK;
 }
@@ -542,13 +554,17 @@ moe_status moe_pack_gate_up_host(const moe_shape *shape, const void *W_g, const 
 {
     MOE_TRY(check_shape(shape));
     if (!W_g || !W_u || !dst) return fail(MOE_ERR_INVALID_ARG, "pack: NULL pointer");
-    const size_t esz = shape->dtype == MOE_DT_BF16 ? 2 : 4;
+    const size_t esz = (size_t)w_esz(*shape);
     const size_t row = (size_t)shape->d * esz;
-    for (int r = 0; r < 2 * shape->f; ++r) {
+    const int f = shape->f;
+    for (int r = 0; r < 2 * f; ++r) {
         const int q = r / 64, w = r % 64;
-        const char *src = w < 32 ? (const char *)W_g + (size_t)(32 * q + w) * row
-                                 : (const char *)W_u + (size_t)(32 * q + w - 32) * row;
+        const int sr = w < 32 ? 32 * q + w : 32 * q + w - 32;   // source row of gate (w < 32) or up
+        const char *src = (const char *)(w < 32 ? W_g : W_u) + (size_t)sr * row;
         memcpy((char *)dst + (size_t)r * row, src, row);
+        if (w_fp8(*shape))   // row scales follow the codes, in the same row order
+            memcpy((char *)dst + (size_t)2 * f * row + (size_t)r * 4,
+                   (const char *)(w < 32 ? W_g : W_u) + (size_t)f * row + (size_t)sr * 4, 4);
     }
     return MOE_OK;
 }
@@ -560,12 +576,11 @@ moe_status moe_arena_create(moe_arena **out, const moe_shape *shape, void *plane
     *out = nullptr;
     MOE_TRY(check_shape(shape));
     if (!plane_gu || !plane_d) return fail(MOE_ERR_INVALID_ARG, "plane is NULL");
-    const int64_t fd = (int64_t)shape->f * shape->d;
-    if (stride_gu < 2 * fd || stride_d < fd)
+    const int esz = w_esz(*shape);
+    if ((size_t)stride_gu * esz < gu_slice_bytes(*shape) || (size_t)stride_d * esz < d_slice_bytes(*shape))
         return fail(MOE_ERR_INVALID_ARG, "slot strides smaller than the slices");
     if (G < 1 || G > shape->P || shape->P % G != 0)
         return fail(MOE_ERR_INVALID_ARG, "need 1 <= G <= P and P %% G == 0");
-    const int esz = shape->dtype == MOE_DT_BF16 ? 2 : 4;
     if (!aligned(plane_gu, 16) || !aligned(plane_d, 16) || (stride_gu * esz) % 16 || (stride_d * esz) % 16)
         return fail(MOE_ERR_INVALID_ARG, "planes and slot strides must be 16-byte aligned");
     moe_arena *a = new moe_arena();
@@ -708,7 +723,7 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
     if (!X || !Y || !arena) return fail(MOE_ERR_INVALID_ARG, "layer: X, Y and arena are required");
     if (!W_r && !logits) return fail(MOE_ERR_INVALID_ARG, "layer: give W_r or logits");
     if (W_r) MOE_TRY(check_router_args(shape, X, W_r));
-    if (!aligned(Y, 16) || (shape->dtype == MOE_DT_BF16 && !aligned(X, 16)))
+    if (!aligned(Y, 16) || (act_bf16(*shape) && !aligned(X, 16)))
         return fail(MOE_ERR_INVALID_ARG, "layer: X and Y must be 16-byte aligned");
     if ((host_gu == nullptr) != (host_d == nullptr))
         return fail(MOE_ERR_INVALID_ARG, "layer: give both host_gu and host_d, or neither");

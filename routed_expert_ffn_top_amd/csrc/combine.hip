@@ -63,19 +63,25 @@ __global__ __launch_bounds__(256) void k_combine(float *__restrict__ Y, int64_t 
 
 // dst row r of expert e: q = r / 64, w = r % 64; gate row 32q + w for w < 32,
 // up row 32q + w - 32 otherwise. One workgroup copies one row as 32-bit words.
+// With row scales (fp8 weights: src_scale_w > 0), the row's fp32 scale moves
+// with it: from word src_scale_w + source row of the source slice to word
+// dst_scale_w + r of the packed slice.
 __global__ __launch_bounds__(256) void k_pack_gate_up(const uint32_t *__restrict__ Wg,
                                                       const uint32_t *__restrict__ Wu,
                                                       uint32_t *__restrict__ dst, int64_t row_words,
-                                                      int64_t src_stride_w, int64_t dst_stride_w)
+                                                      int64_t src_stride_w, int64_t dst_stride_w,
+                                                      int64_t src_scale_w, int64_t dst_scale_w)
 {
     const int r = blockIdx.x;
     const int e = blockIdx.y;
     const int q = r >> 6, w = r & 63;
-    const uint32_t *src = (w < 32 ? Wg + (int64_t)(32 * q + w) * row_words
-                                  : Wu + (int64_t)(32 * q + w - 32) * row_words) +
-                          (int64_t)e * src_stride_w;
+    const int sr = w < 32 ? 32 * q + w : 32 * q + w - 32;
+    const uint32_t *slice = (w < 32 ? Wg : Wu) + (int64_t)e * src_stride_w;
+    const uint32_t *src = slice + (int64_t)sr * row_words;
     uint32_t *out = dst + (int64_t)e * dst_stride_w + (int64_t)r * row_words;
     for (int64_t c = threadIdx.x; c < row_words; c += 256) out[c] = src[c];
+    if (src_scale_w > 0 && threadIdx.x == 0)
+        dst[(int64_t)e * dst_stride_w + dst_scale_w + r] = slice[src_scale_w + sr];
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -135,12 +141,15 @@ hipError_t launch_pack_gate_up(const moe_shape &s, const void *Wg, const void *W
                                int n, int64_t src_stride, int64_t dst_stride, hipStream_t st)
 {
     if (n == 0) return hipSuccess;
-    const int esz = s.dtype == MOE_DT_BF16 ? 2 : 4;
+    const int esz = w_esz(s);
     const int64_t row_words = (int64_t)s.d * esz / 4;
     const int64_t ssw = src_stride * esz / 4, dsw = dst_stride * esz / 4;
+    // fp8: the row scales follow the codes ([f] after [f][d], [2f] after [2f][d])
+    const int64_t sscale = w_fp8(s) ? (int64_t)s.f * row_words : 0;
+    const int64_t dscale = w_fp8(s) ? (int64_t)2 * s.f * row_words : 0;
     hipLaunchKernelGGL(k_pack_gate_up, dim3((unsigned)(2 * s.f), (unsigned)n), dim3(256), 0, st,
                        (const uint32_t *)Wg, (const uint32_t *)Wu, (uint32_t *)dst, row_words, ssw,
-                       dsw);
+                       dsw, sscale, dscale);
     return hipGetLastError();
 }
 

@@ -33,6 +33,22 @@ struct WsLayout {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Element formats. MOE_DT_BF16_FP8W: bf16 activations, fp8 e4m3 expert
+// weights with one fp32 scale per weight row (a slot slice holds the codes,
+// then the scales).
+inline bool act_bf16(const moe_shape &s) { return s.dtype == MOE_DT_BF16 || s.dtype == MOE_DT_BF16_FP8W; }
+inline bool w_fp8(const moe_shape &s) { return s.dtype == MOE_DT_BF16_FP8W; }
+inline int w_esz(const moe_shape &s) { return s.dtype == MOE_DT_F32 ? 4 : (s.dtype == MOE_DT_BF16 ? 2 : 1); }
+// bytes of one expert's packed gate/up slice and down slice (codes + scales for fp8)
+inline size_t gu_slice_bytes(const moe_shape &s)
+{
+    return (size_t)2 * s.f * s.d * w_esz(s) + (w_fp8(s) ? (size_t)2 * s.f * 4 : 0);
+}
+inline size_t d_slice_bytes(const moe_shape &s)
+{
+    return (size_t)s.d * s.f * w_esz(s) + (w_fp8(s) ? (size_t)s.d * 4 : 0);
+}
+
 // Splits of the down projection's K = f: when the down tiles (about
 // experts x row blocks x d/256) would not fill the GPU, each tile's K range
 // is cut in S pieces whose partial products go to S separate per-route rows,
@@ -40,7 +56,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // <= 512 and f splits into multiples of 64; at most 4.
 inline int down_splits(const moe_shape &s)
 {
-    if (s.dtype != MOE_DT_BF16) return 1;
+    if (!act_bf16(s)) return 1;
     const int64_t ne = s.E + s.n_shared;
     const int64_t per = ((int64_t)s.T * (s.k + s.n_shared) + ne - 1) / ne;
     const int64_t tiles = ne * ((per + 255) / 256) * ((s.d + 255) / 256);
@@ -53,7 +69,7 @@ inline WsLayout ws_layout(const moe_shape &s)
 {
     WsLayout w{};
     const size_t kp = (size_t)(s.k + s.n_shared);
-    const size_t esz = s.dtype == MOE_DT_BF16 ? 2 : 4;
+    const size_t esz = act_bf16(s) ? 2 : 4;   // H holds activations
     w.nblk = (s.capacity + kRouteBlock - 1) / kRouteBlock;
     size_t o = 0;
     w.err = o;    o = align_up(o + 64 * 4, 256);
@@ -80,7 +96,9 @@ struct GemmArgs {
     const void *A;               // X (gate/up) or H (down)
     int64_t lda;                 // ldx or f
     const void *B;               // plane base
-    int64_t slot_stride;         // elements
+    int64_t slot_stride;         // elements (bytes for fp8 weights)
+    int bfp8;                    // B: fp8 e4m3 codes with fp32 row scales
+    int64_t scale_off;           // fp8: bytes from a slot slice's start to its row scales
     int N, K;
     void *C;                     // H (gate/up) or Yr (down)
     int64_t ldc;                 // f or d

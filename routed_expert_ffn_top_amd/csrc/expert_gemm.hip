@@ -32,6 +32,19 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// Eight fp8 e4m3 codes (bytes 0..7 of w) to eight bf16 values, in order; exact
+// (scale 1), two codes per v_cvt_scalef32_pk_bf16_fp8.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(u32x2_t w)
+{
+    const bf16x2v_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.0f, false);
+    const bf16x2v_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.0f, true);
+    const bf16x2v_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.0f, false);
+    const bf16x2v_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.0f, true);
+    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
 
 struct TileInfo {
     int slot, row0, rows, n0, ks;   // ks: which of the a.splits K ranges
@@ -191,23 +204,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-template <int BM, int BN, int NS, int WM, int WN, bool GATEUP>
+// BF8: the weights (B) are fp8 e4m3 codes with one fp32 scale per weight row
+// (the slot slice holds the codes, then the row scales, a.scale_off bytes in).
+// B rows then take 32 bytes per stage; each wave's fragments are converted to
+// bf16 (exactly: every e4m3 value is a bf16 value) just before its MFMAs, and
+// the row scales multiply the fp32 accumulators in the epilogue.
+template <int BM, int BN, int NS, int WM, int WN, bool GATEUP, bool BF8>
 __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
 {
     constexpr int NW = WM * WN, NT = NW * 64;
-    constexpr int BK = 32, ROWB = 64;                   // bytes per LDS row (32 bf16)
+    constexpr int BK = 32, ROWB = 64;                   // bytes per LDS row of A (32 bf16)
+    constexpr int BROW = BF8 ? 32 : 64;                 // bytes per LDS row of B (32 codes or 32 bf16)
+    constexpr int BESZ = BF8 ? 1 : 2;                   // bytes per B element
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MI = TM / 32, NI = TN / 32;
-    constexpr int STAGE = (BM + BN) * ROWB;             // bytes per stage
-    constexpr int AI = BM / 16 / NW, BI = BN / 16 / NW; // 1 KB copies per wave per stage
+    constexpr int STAGE = BM * ROWB + BN * BROW;        // bytes per stage
+    constexpr int AI = BM / 16 / NW, BI = BN * BROW / 1024 / NW; // 1 KB copies per wave per stage
     constexpr int LOADS = AI + BI;
-    static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0 && MI >= 1 && NI >= 1, "tile");
+    static_assert(BM % (16 * NW) == 0 && (BN * BROW) % (1024 * NW) == 0 && MI >= 1 && NI >= 1, "tile");
     static_assert(!GATEUP || (TN % 64) == 0, "gate/up pairs need 64-column wave tiles");
     static_assert(NS >= 3, "the ring needs at least 3 stages");
 
     __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
     __shared__ int32_t s_route[2][GATEUP ? 1 : BM];   // by tile parity
     __shared__ float s_alpha[2][GATEUP ? 1 : BM];
+    __shared__ float s_scale[2][BF8 ? BN : 1];          // row scales of the tile's B rows, by parity
     __shared__ int32_t s_tpref[kMaxExp + 1];           // first logical tile of each slot
     __shared__ int32_t s_off[kMaxExp + 1];
 
@@ -290,13 +311,22 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
             const int c = lp ^ ((r >> 2) & 3);
             asrc[j] = (const char *)a.A + ((int64_t)rows[j] * a.lda + (int64_t)t.ks * Kc) * 2 + c * 16;
         }
-        const char *Bslot = (const char *)a.B + (int64_t)t.slot * a.slot_stride * 2;
+        const char *Bslot = (const char *)a.B + (int64_t)t.slot * a.slot_stride * BESZ;
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
-            const int r = (wave * BI + j) * 16 + lr;
-            const int c = lp ^ ((r >> 2) & 3);
-            const int n = min(t.n0 + r, N - 1);
-            bsrc[j] = Bslot + ((int64_t)n * K + (int64_t)t.ks * Kc) * 2 + c * 16;
+            if constexpr (BF8) {
+                // 32 rows of 32 bytes per instruction: lane -> row l/2, and the
+                // 16-byte half (l%2) ^ ((row >> 3) & 1) of it
+                const int r = (wave * BI + j) * 32 + (lane >> 1);
+                const int c = (lane & 1) ^ ((r >> 3) & 1);
+                const int n = min(t.n0 + r, N - 1);
+                bsrc[j] = Bslot + (int64_t)n * K + (int64_t)t.ks * Kc + c * 16;
+            } else {
+                const int r = (wave * BI + j) * 16 + lr;
+                const int c = lp ^ ((r >> 2) & 3);
+                const int n = min(t.n0 + r, N - 1);
+                bsrc[j] = Bslot + ((int64_t)n * K + (int64_t)t.ks * Kc) * 2 + c * 16;
+            }
         }
     };
     // down: route id and alpha of tile row tid (threads tid < BM), staged in
@@ -310,11 +340,20 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     auto fetch_alpha = [&]() {
         if (!GATEUP && tid < BM) pre_al = a.topk_w[pre_rt];
     };
+    // fp8 weights: the scale of B row n0 + tid (threads tid < BN)
+    float pre_sc = 0.0f;
+    auto fetch_scale = [&](const TileInfo &t) {
+        if (BF8 && tid < BN) {
+            const char *Bslot = (const char *)a.B + (int64_t)t.slot * a.slot_stride;
+            pre_sc = *(const float *)(Bslot + a.scale_off + (int64_t)min(t.n0 + tid, N - 1) * 4);
+        }
+    };
     auto store_routes = [&](int par) {
         if (!GATEUP && tid < BM) {
             s_route[par][tid] = pre_rt;
             s_alpha[par][tid] = pre_al;
         }
+        if (BF8 && tid < BN) s_scale[par][tid] = pre_sc;
     };
     auto issue = [&](int kt) {
         char *st = lds + (kt % NS) * STAGE;
@@ -325,7 +364,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                                              (LDS_AS void *)(st + (wave * AI + j) * 1024), 16, 0, 0);
 #pragma unroll
         for (int j = 0; j < BI; ++j)
-            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(bsrc[j] + kb),
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(bsrc[j] + kt * BK * BESZ),
                                              (LDS_AS void *)(st + BM * ROWB + (wave * BI + j) * 1024), 16, 0,
                                              0);
     };
@@ -337,15 +376,31 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                          (lane & 31) * ROWB + ((2 + (lane >> 5)) ^ sw) * 16};
     f32x16_t acc[MI][NI];
     bf16x8_t af[2][MI], bfr[2][NI];
+    u32x2_t braw[2][NI];   // fp8 weights: 8 codes per fragment, converted in mfmas
+    // fp8 fragment of B row (lane & 31): 8-byte piece c = 2*ks + (lane >> 5) of
+    // the 32-byte row, stored in 16-byte half (c >> 1) ^ ((row >> 3) & 1)
+    const int br8 = lane & 31;
+    const int boff8[2] = {br8 * 32 + (((0 + (lane >> 5)) >> 1 ^ ((br8 >> 3) & 1)) << 4) + (((0 + (lane >> 5)) & 1) << 3),
+                          br8 * 32 + (((2 + (lane >> 5)) >> 1 ^ ((br8 >> 3) & 1)) << 4) + (((2 + (lane >> 5)) & 1) << 3)};
     auto read_frags = [&](int stage, int ks, int set) {
         const char *As = lds + stage * STAGE + wm * TM * ROWB + foff[ks];
-        const char *Bs = lds + stage * STAGE + BM * ROWB + wn * TN * ROWB + foff[ks];
 #pragma unroll
         for (int i = 0; i < MI; ++i) af[set][i] = *(const bf16x8_t *)(As + i * 32 * ROWB);
+        if constexpr (BF8) {
+            const char *Bs = lds + stage * STAGE + BM * ROWB + wn * TN * BROW + boff8[ks];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) bfr[set][j] = *(const bf16x8_t *)(Bs + j * 32 * ROWB);
+            for (int j = 0; j < NI; ++j) braw[set][j] = *(const u32x2_t *)(Bs + j * 32 * BROW);
+        } else {
+            const char *Bs = lds + stage * STAGE + BM * ROWB + wn * TN * ROWB + foff[ks];
+#pragma unroll
+            for (int j = 0; j < NI; ++j) bfr[set][j] = *(const bf16x8_t *)(Bs + j * 32 * ROWB);
+        }
     };
     auto mfmas = [&](int set) {
+        if constexpr (BF8) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) bfr[set][j] = fp8x8_to_bf16(braw[set][j]);
+        }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -370,6 +425,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     fetch_rows(cur, rows);
     set_sources(cur, rows);
     fetch_route(cur);
+    fetch_scale(cur);
     fetch_alpha();
     store_routes(0);
 #pragma unroll
@@ -426,6 +482,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
             if (has_next && kt == 0) {
                 fetch_rows(nxt, rows);
                 fetch_route(nxt);
+                fetch_scale(nxt);
             }
             if (has_next && kt == 1) fetch_alpha();
             if (more && kt + NS - 1 < nk) issue(kt + NS - 1);
@@ -464,6 +521,10 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         const bool even = (lane & 1) == 0;
         const int cpair = (lane & 31) & ~1;
         const bool full = cur.rows == BM && cur.n0 + BN <= N;
+        // fp8 weights: the row scale of each of this lane's accumulator columns
+        float sc[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) sc[j] = BF8 ? s_scale[par][wn * TN + j * 32 + (lane & 31)] : 1.0f;
         auto epilogue = [&](auto checked_t) {
             constexpr bool checked = decltype(checked_t)::value;
             if constexpr (GATEUP) {
@@ -478,8 +539,10 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                         uint16_t *hrow = H + (int64_t)(cur.row0 + (checked ? min(m, cur.rows - 1) : m)) * a.ldc + fc0;
 #pragma unroll
                         for (int q = 0; q < NI / 2; ++q) {
-                            const float s0 = silu_mul_fast(acc[i][2 * q][r], acc[i][2 * q + 1][r]);
-                            const float s1 = silu_mul_fast(acc[i][2 * q][r + 1], acc[i][2 * q + 1][r + 1]);
+                            const float s0 = BF8 ? silu_mul_fast(acc[i][2 * q][r] * sc[2 * q], acc[i][2 * q + 1][r] * sc[2 * q + 1])
+                                                 : silu_mul_fast(acc[i][2 * q][r], acc[i][2 * q + 1][r]);
+                            const float s1 = BF8 ? silu_mul_fast(acc[i][2 * q][r + 1] * sc[2 * q], acc[i][2 * q + 1][r + 1] * sc[2 * q + 1])
+                                                 : silu_mul_fast(acc[i][2 * q][r + 1], acc[i][2 * q + 1][r + 1]);
                             const float y = __int_as_float(
                                 __builtin_amdgcn_mov_dpp(__float_as_int(even ? s1 : s0), 0xB1, 0xF, 0xF, false));
                             const uint32_t packed = even ? pack_bf16x2(s0, y) : pack_bf16x2(y, s1);
@@ -504,7 +567,8 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                         const float al = s_alpha[par][mc];
 #pragma unroll
                         for (int j = 0; j < NI; ++j)
-                            if (!checked || (m < cur.rows && ncol + j * 32 < N)) yrow[j * 32] = al * acc[i][j][r];
+                            if (!checked || (m < cur.rows && ncol + j * 32 < N))
+                                yrow[j * 32] = BF8 ? al * (acc[i][j][r] * sc[j]) : al * acc[i][j][r];
                     }
                 }
             }
@@ -641,7 +705,12 @@ hipError_t launch_mfma_lds(const GemmArgs &a, int max_rows, hipStream_t st)
     // never more than there can be tiles
     const unsigned g = std::min<unsigned>(grid_bound(a, max_rows, BM, BN), (unsigned)device_cus());
     if (g == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP>), dim3(g), dim3(WM * WN * 64), 0, st, a);
+    if (a.bfp8)
+        hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, true>), dim3(g), dim3(WM * WN * 64), 0,
+                           st, a);
+    else
+        hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, false>), dim3(g), dim3(WM * WN * 64), 0,
+                           st, a);
     return hipGetLastError();
 }
 
@@ -668,7 +737,10 @@ hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, b
 {
     if (max_rows == 0) return hipSuccess;
     if (s.dtype == MOE_DT_F32) return launch_simple<float, true>(a, max_rows, st);
-    if (simple) return launch_simple<uint16_t, true>(a, max_rows, st);
+    if (simple) {
+        if (a.bfp8) return hipErrorInvalidValue;   // the plain kernel reads bf16 weights only
+        return launch_simple<uint16_t, true>(a, max_rows, st);
+    }
     return launch_mfma_lds<MOE_RING_TILE, true>(a, max_rows, st);
 }
 
@@ -677,7 +749,10 @@ hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool
 {
     if (max_rows == 0) return hipSuccess;
     if (s.dtype == MOE_DT_F32) return launch_simple<float, false>(a, max_rows, st);
-    if (simple) return launch_simple<uint16_t, false>(a, max_rows, st);
+    if (simple) {
+        if (a.bfp8) return hipErrorInvalidValue;
+        return launch_simple<uint16_t, false>(a, max_rows, st);
+    }
     return launch_mfma_lds<MOE_RING_TILE, false>(a, max_rows, st);
 }
 

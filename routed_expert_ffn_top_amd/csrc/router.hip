@@ -398,7 +398,7 @@ hipError_t launch_router_logits(const moe_shape &s, const void *X, const float *
 #ifdef MOE_ROUTER_NE
     ne = MOE_ROUTER_NE;
 #endif
-    if (s.dtype == MOE_DT_BF16) {
+    if (act_bf16(s)) {
         if (ne == 4) return launch_router_t<uint16_t, 4>(s, X, Wr, bias, L, st);
         if (ne == 2) return launch_router_t<uint16_t, 2>(s, X, Wr, bias, L, st);
         return launch_router_t<uint16_t, 1>(s, X, Wr, bias, L, st);

@@ -26,6 +26,13 @@ and the oracle see exactly the same numbers. The router weight stays fp32.
 
 Weight layout is nn.Linear style ([out, in]): W_gate, W_up [n_exp, f, d],
 W_down [n_exp, d, f], with n_exp = E + n_shared (shared experts last).
+
+Weight-only quantised workloads (dtype ``bf16_fp8w``, names ending in
+``_fp8w``): the same fp32 weight draws are stored per output row as fp8 e4m3
+codes and one fp32 scale, scale = max|row| / 448 (the largest e4m3 value),
+codes = row / scale rounded to nearest even by PyTorch's float8_e4m3fn
+conversion. The quantised model is then the model under test: both sides get
+the codes and the scales.
 """
 from __future__ import annotations
 
@@ -47,7 +54,8 @@ class MoEConfig:
     k: int
     f: int
     n_shared: int = 0
-    dtype: str = "bf16"          # "bf16" or "f32": X, expert weights, H
+    dtype: str = "bf16"          # "bf16", "f32" (X, expert weights, H), or "bf16_fp8w"
+                                 # (bf16 X and H, fp8 e4m3 weights with row scales)
     renorm: bool = True          # renormalise the top-k softmax weights
     zipf: bool = False           # Zipf(1.1) popularity bias on the logits
     P: Optional[int] = None      # arena slots (None: one slot per expert)
@@ -69,7 +77,12 @@ class MoEConfig:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        """Element type of the activations (and of unquantised weights)."""
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def fp8_weights(self) -> bool:
+        return self.dtype == "bf16_fp8w"
 
     def with_(self, **kw) -> "MoEConfig":
         return dataclasses.replace(self, **kw)
@@ -99,6 +112,11 @@ CONFIGS = {
 for _t in (256, 512, 1024, 2048, 4096):
     CONFIGS[f"virt_olmoe_t{_t}"] = _cfg(f"virt_olmoe_t{_t}", 5, T=_t, d=2048,
                                         E=64, k=8, f=1024, zipf=True, P=16, G=8)
+# the same workloads with fp8 e4m3 weights (same seeds: same X, router and
+# weight draws before quantisation)
+for _n in ("olmoe_t1024", "olmoe_t4096", "dsv2lite_t4096", "mixtral_t256", "mixtral_t1024",
+           "mixtral_t4096", "virt_olmoe_t256", "virt_olmoe_t1024", "virt_olmoe_t4096"):
+    CONFIGS[_n + "_fp8w"] = CONFIGS[_n].with_(name=_n + "_fp8w", dtype="bf16_fp8w")
 
 
 def seed_for(cfg: MoEConfig, layer: int = 0) -> int:
@@ -115,11 +133,30 @@ class LayerInputs:
     Wu: torch.Tensor              # [n_exp, f, d] cfg dtype
     Wd: torch.Tensor              # [n_exp, d, f] cfg dtype
     A: torch.Tensor               # [T, d]        fp32 residual
+    # fp8 weights: Wg, Wu, Wd hold e4m3 codes (uint8) and these the row scales
+    Sg: Optional[torch.Tensor] = None   # [n_exp, f] fp32
+    Su: Optional[torch.Tensor] = None   # [n_exp, f] fp32
+    Sd: Optional[torch.Tensor] = None   # [n_exp, d] fp32
 
     def to(self, device) -> "LayerInputs":
         mv = lambda t: None if t is None else t.to(device)
         return LayerInputs(self.cfg, mv(self.X), mv(self.Wr), mv(self.bias),
-                           mv(self.Wg), mv(self.Wu), mv(self.Wd), mv(self.A))
+                           mv(self.Wg), mv(self.Wu), mv(self.Wd), mv(self.A),
+                           mv(self.Sg), mv(self.Su), mv(self.Sd))
+
+
+E4M3_MAX = 448.0
+
+
+def quantize_rows_e4m3(W: torch.Tensor):
+    """Per-row fp8 e4m3 storage of W [..., rows, cols] (fp32): returns
+    (codes uint8 [..., rows, cols], scales fp32 [..., rows]) with
+    scale = max|row| / 448 (1 for an all-zero row) and codes the e4m3
+    encoding of row / scale (round to nearest even)."""
+    amax = W.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).to(torch.float32)
+    codes = (W / scale.unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
 
 
 def _normal(gen, shape, std, device):
@@ -147,15 +184,20 @@ def make_inputs(cfg: MoEConfig, layer: int = 0, device="cpu",
     X = _normal(gen, (cfg.T, cfg.d), 1.0, device).to(dt)
     Wr = _normal(gen, (cfg.d, cfg.E), STD_W, device)
     ne = cfg.n_exp
-    Wg = _normal(gen, (ne, cfg.f, cfg.d), STD_W, device).to(dt)
-    Wu = _normal(gen, (ne, cfg.f, cfg.d), STD_W, device).to(dt)
-    Wd = _normal(gen, (ne, cfg.d, cfg.f), STD_W, device).to(dt)
+    Wg = _normal(gen, (ne, cfg.f, cfg.d), STD_W, device)
+    Wu = _normal(gen, (ne, cfg.f, cfg.d), STD_W, device)
+    Wd = _normal(gen, (ne, cfg.d, cfg.f), STD_W, device)
+    Sg = Su = Sd = None
+    if cfg.fp8_weights:
+        (Wg, Sg), (Wu, Su), (Wd, Sd) = (quantize_rows_e4m3(w) for w in (Wg, Wu, Wd))
+    else:
+        Wg, Wu, Wd = Wg.to(dt), Wu.to(dt), Wd.to(dt)
     if residual:
         A = _normal(gen, (cfg.T, cfg.d), 1.0, device)
     else:
         A = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device=device)
     bias = zipf_bias(cfg, gen, device) if cfg.zipf else None
-    return LayerInputs(cfg, X, Wr, bias, Wg, Wu, Wd, A)
+    return LayerInputs(cfg, X, Wr, bias, Wg, Wu, Wd, A, Sg, Su, Sd)
 
 
 def make_logits(T: int, E: int, seed: int, scale: float = 1.0,
@@ -191,6 +233,6 @@ def rows_per_slot_stats(counts) -> dict:
             "mean": (sum(c) / len(c)) if c else 0.0}
 
 
-__all__ = ["MoEConfig", "CONFIGS", "LayerInputs", "make_inputs", "make_logits",
+__all__ = ["MoEConfig", "CONFIGS", "LayerInputs", "make_inputs", "make_logits", "quantize_rows_e4m3",
            "seed_for", "identity_phi", "random_phi", "zipf_bias", "STD_W",
            "rows_per_slot_stats"]

@@ -49,22 +49,28 @@ class MoELayer:
         Wg = inp.Wg.to(self.device)
         Wu = inp.Wu.to(self.device)
         Wd = inp.Wd.to(self.device)
+        scales = None
+        if cfg.fp8_weights:
+            scales = tuple(t.to(self.device) for t in (inp.Sg, inp.Su, inp.Sd))
         if paged:
             # prepacked experts in two pinned host planes, expert after expert,
             # so that consecutive experts load with one transfer per plane
-            self.host_gu_plane = torch.empty((ne, 2 * cfg.f, cfg.d), dtype=Wg.dtype, pin_memory=True)
-            self.host_d_plane = torch.empty((ne, cfg.d, cfg.f), dtype=Wd.dtype, pin_memory=True)
-            tmp = torch.empty((2 * cfg.f, cfg.d), dtype=Wg.dtype, device=self.device)
+            gu_shape = tuple(self.arena.plane_gu.shape[1:])
+            d_shape = tuple(self.arena.plane_d.shape[1:])
+            self.host_gu_plane = torch.empty((ne,) + gu_shape, dtype=self.arena.plane_gu.dtype, pin_memory=True)
+            self.host_d_plane = torch.empty((ne,) + d_shape, dtype=self.arena.plane_d.dtype, pin_memory=True)
+            tmp = torch.empty(gu_shape, dtype=self.arena.plane_gu.dtype, device=self.device)
             for e in range(ne):
-                B.moe_pack_gate_up(self.shape, Wg[e], Wu[e], tmp, 1, 0, 0, stream)
+                g, u, dn = B.expert_slices(Wg, Wu, Wd, scales, e)
+                B.moe_pack_gate_up(self.shape, g, u, tmp, 1, 0, 0, stream)
                 self.host_gu_plane[e].copy_(tmp)
-                self.host_d_plane[e].copy_(Wd[e])
+                self.host_d_plane[e].copy_(dn.reshape(d_shape))
             self.host_gu = [self.host_gu_plane[e] for e in range(ne)]
             self.host_d = [self.host_d_plane[e] for e in range(ne)]
             self.phi = None
         else:
             self.phi = list(range(ne)) if phi is None else [int(x) for x in phi]
-            self.arena.load_resident(Wg, Wu, Wd, self.phi, stream)
+            self.arena.load_resident(Wg, Wu, Wd, self.phi, stream, scales=scales)
             self.host_gu = self.host_d = None
         torch.cuda.synchronize(self.device)
 

@@ -11,7 +11,7 @@ from oracle import oracle as oracle_mod
 from routed_expert_ffn_top_amd import binding as B
 from routed_expert_ffn_top_amd.inputs import LayerInputs, MoEConfig, make_inputs
 
-TOL = {"bf16": 1e-2, "f32": 1e-5}
+TOL = {"bf16": 1e-2, "f32": 1e-5, "bf16_fp8w": 1e-2}
 ALPHA_TOL = 1e-6
 
 
@@ -48,8 +48,17 @@ class OracleRun:
         self._inp = inp
 
     def weights(self):
+        """Weights as the oracle takes them; fp8 codes are decoded by the
+        oracle itself and come with their row scales."""
         if self._w is None:
-            self._w = (np32(self._inp.Wg), np32(self._inp.Wu), np32(self._inp.Wd))
+            inp = self._inp
+            if self.cfg.fp8_weights:
+                dec = lambda q: self.orc.fp8e4m3_decode(q.cpu().numpy())
+                self._w = (dec(inp.Wg), dec(inp.Wu), dec(inp.Wd))
+                self._scales = (np32(inp.Sg), np32(inp.Su), np32(inp.Sd))
+            else:
+                self._w = (np32(inp.Wg), np32(inp.Wu), np32(inp.Wd))
+                self._scales = None
         return self._w
 
     def route_map(self, phi, P, t0=0, nt=None):
@@ -58,7 +67,7 @@ class OracleRun:
     def Y(self, tokens=None, route_mask=None):
         Wg, Wu, Wd = self.weights()
         return self.orc.expert_ffn(self.X, self.idx, self.alpha, Wg, Wu, Wd, self.A,
-                                   tokens=tokens, route_mask=route_mask)
+                                   tokens=tokens, route_mask=route_mask, scales=self._scales)
 
 
 def check_descriptors(routes: dict, ref: dict, n_valid_expected=None):

@@ -144,6 +144,42 @@ def test_pack_gate_up_host_layout():
     assert torch.equal(outb[32:64], Wu[:32].bfloat16())
 
 
+def test_pack_gate_up_host_fp8_rows_and_scales():
+    """fp8 weights: the packed slice is the permuted code rows followed by
+    the rows' fp32 scales in the same permuted order."""
+    f, d = 128, 64
+    s = B.make_shape(T=4, d=d, f=f, E=4, k=1, dtype="bf16_fp8w")
+    assert B.moe_workspace_bytes(s) > 0
+    rng = np.random.default_rng(1)
+    codes_g = rng.integers(0, 256, size=(f, d), dtype=np.uint8)
+    codes_u = rng.integers(0, 256, size=(f, d), dtype=np.uint8)
+    sc_g = rng.random(f, dtype=np.float32)
+    sc_u = rng.random(f, dtype=np.float32)
+    src_g = torch.from_numpy(np.concatenate([codes_g.reshape(-1), sc_g.view(np.uint8)]))
+    src_u = torch.from_numpy(np.concatenate([codes_u.reshape(-1), sc_u.view(np.uint8)]))
+    out = torch.empty(2 * f * d + 8 * f, dtype=torch.uint8)
+    B.moe_pack_gate_up_host(s, src_g, src_u, out)
+    o = out.numpy()
+    rows = o[:2 * f * d].reshape(2 * f, d)
+    scales = o[2 * f * d:].view(np.float32)
+    for q in range(f // 32):
+        assert np.array_equal(rows[64 * q:64 * q + 32], codes_g[32 * q:32 * q + 32])
+        assert np.array_equal(rows[64 * q + 32:64 * q + 64], codes_u[32 * q:32 * q + 32])
+        assert np.array_equal(scales[64 * q:64 * q + 32], sc_g[32 * q:32 * q + 32])
+        assert np.array_equal(scales[64 * q + 32:64 * q + 64], sc_u[32 * q:32 * q + 32])
+
+
+def test_arena_fp8_strides_are_bytes_and_cover_the_scales():
+    f, d = 256, 128
+    s = B.make_shape(T=16, d=d, f=f, E=8, k=2, P=4, dtype="bf16_fp8w")
+    gu, dn = 2 * f * d + 8 * f, d * f + 4 * d
+    with pytest.raises(B.MoEError):   # codes only, no room for the scales
+        B.moe_arena_create(s, 0x100000, 0x40000000, 2 * f * d, dn, 2)
+    with pytest.raises(B.MoEError):
+        B.moe_arena_create(s, 0x100000, 0x40000000, gu, d * f, 2)
+    B.moe_arena_destroy(B.moe_arena_create(s, 0x100000, 0x40000000, gu, dn, 2))
+
+
 class _FakeArena:
     def __init__(self, handle):
         self.handle = handle

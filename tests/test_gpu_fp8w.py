@@ -1,0 +1,107 @@
+"""Parity of the weight-only quantised layer (fp8 e4m3 expert weights with
+fp32 row scales, bf16 activations) with the CPU oracle.
+
+The oracle decodes the same e4m3 codes from the format's definition and
+applies the same row scales in fp64. Tolerances are those of the bf16 layer:
+max|y - y_ref| / max|y_ref| <= 1e-2; routing, descriptors and run-to-run bits
+are exact as for every other layer.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import OracleRun, TOL, gpu_inputs, np32, rel_err, sample_tokens, say
+from routed_expert_ffn_top_amd import binding as B
+from routed_expert_ffn_top_amd.inputs import CONFIGS
+from routed_expert_ffn_top_amd.layer import MoELayer
+from test_gpu_parity import MID, MID_SHARED, _check_layer, _layer_out
+
+pytestmark = pytest.mark.gpu
+
+MID8 = MID.with_(name="mid_fp8w", dtype="bf16_fp8w")
+MID8_SHARED = MID_SHARED.with_(name="mid_shared_fp8w", dtype="bf16_fp8w")
+
+
+def test_layer_mid_fp8w():
+    say("layer mid, fp8 weights")
+    _check_layer(MID8)
+
+
+def test_layer_shared_experts_fp8w():
+    say("layer with shared experts, fp8 weights")
+    _check_layer(MID8_SHARED)
+
+
+def test_layer_olmoe_t4096_fp8w_sampled():
+    say("layer OLMoE T=4096, fp8 weights (sampled rows)")
+    cfg = CONFIGS["olmoe_t4096_fp8w"]
+    _check_layer(cfg, tokens=sample_tokens(cfg.T, 96))
+
+
+def test_layer_mixtral_t256_fp8w_sampled():
+    say("layer Mixtral T=256, fp8 weights, split-K down (sampled rows)")
+    cfg = CONFIGS["mixtral_t256_fp8w"]
+    _check_layer(cfg, tokens=sample_tokens(cfg.T, 24))
+
+
+def test_fp8w_step_by_step_and_capacity_split():
+    say("fp8 weights: separate calls and a capacity split give the same bits")
+    inp = gpu_inputs(MID8)
+    layer = MoELayer(inp)
+    y1 = _layer_out(layer, inp)
+    s = layer.shape
+    L = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    B.moe_router_logits(s, layer.X, layer.Wr, layer.bias, L)
+    B.moe_route_build(s, 0, s.T, L, layer.phi, 0, layer.routes, layer.ws)
+    y2 = inp.A.clone()
+    B.moe_expert_ffn(s, layer.X, y2, layer.routes, layer.arena, layer.phi,
+                     B.MOE_FFN_EXPERTS | B.MOE_FFN_FINALIZE, layer.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    split = MoELayer(inp, capacity=(MID8.T * MID8.kp) // 3 + 5)
+    assert torch.equal(_layer_out(split, inp), y1)
+
+
+def test_fp8w_plain_kernel_rejected():
+    say("fp8 weights: the plain bf16 kernel is refused")
+    inp = gpu_inputs(MID8)
+    layer = MoELayer(inp)
+    s = layer.shape
+    L = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    B.moe_router_logits(s, layer.X, layer.Wr, layer.bias, L)
+    B.moe_route_build(s, 0, s.T, L, layer.phi, 0, layer.routes, layer.ws)
+    Y = inp.A.clone()
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_expert_ffn(s, layer.X, Y, layer.routes, layer.arena, layer.phi,
+                         B.MOE_FFN_EXPERTS | B.MOE_FFN_SIMPLE_KERNEL, layer.ws)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+
+
+def test_paged_equals_resident_fp8w():
+    say("paged layer with fp8 weights (P=16, G=8) vs resident")
+    cfg = CONFIGS["virt_olmoe_t256_fp8w"]
+    inp = gpu_inputs(cfg)
+    res = MoELayer(inp)
+    y_res = _layer_out(res, inp)
+    res.close()
+    paged = MoELayer(inp, paged=True)
+    copy = torch.cuda.Stream()
+    for _ in range(2):                   # the arena is reused by the second call
+        Y = inp.A.clone()
+        paged.forward(Y, copy=copy)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, y_res), "paging changed the output"
+    orun = OracleRun(inp)
+    toks = sample_tokens(cfg.T, 48)
+    assert rel_err(np32(Y)[toks], orun.Y(tokens=toks)) <= TOL[cfg.dtype]
+
+
+def test_fp8w_quantisation_error_is_small():
+    say("fp8 weights vs the bf16 layer of the same draws")
+    i8, ib = gpu_inputs(MID8), gpu_inputs(MID)
+    assert torch.equal(i8.A, ib.A) and torch.equal(i8.X, ib.X)
+    f8 = np32(_layer_out(MoELayer(i8), i8) - i8.A)      # the FFN part of the output
+    fb = np32(_layer_out(MoELayer(ib), ib) - ib.A)
+    d = rel_err(f8, fb.astype(np.float64))
+    say(f"  rel diff fp8 vs bf16 weights: {d:.3e}")
+    assert d < 0.1
