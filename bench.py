@@ -57,6 +57,10 @@ for _t in (256, 1024, 4096):
     WORKLOAD_TEXT[f"mixtral_stack_t{_t}"] = (
         f"32 Mixtral-8x7B-shaped MoE layers with independent weights, all resident (90.2 GB): T={_t}, "
         "d=4096, E=8, top-2 renormalised, SwiGLU f=14336, bf16; only the MoE sublayers are timed")
+for _n in list(WORKLOAD_TEXT):
+    WORKLOAD_TEXT[_n + "_fp8w"] = (WORKLOAD_TEXT[_n].replace(", bf16", ", bf16 activations")
+                                   + "; expert weights stored as fp8 e4m3 codes with one fp32 scale per row "
+                                   "(weight-only quantisation, decoded to bf16 MFMA operands)")
 PCIE_GEN5_X16_GBS = 64.0   # one direction, before protocol overhead
 
 
@@ -196,6 +200,14 @@ def torch_bmm_expert_shape(torch, cfg, reps=10) -> dict:
     return out
 
 
+def expert_slice_bytes(cfg) -> int:
+    """Bytes of one expert's gate/up and down slices (fp8: codes plus the
+    fp32 row scales)."""
+    if cfg.fp8_weights:
+        return 3 * cfg.d * cfg.f + (2 * cfg.f + cfg.d) * 4
+    return 3 * cfg.d * cfg.f * (4 if cfg.dtype == "f32" else 2)
+
+
 def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
     """The CPU oracle (as it stands) on the same workload: routing for every
     token, the expert FFN on a token sample sized to ~target_s seconds,
@@ -207,7 +219,13 @@ def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
     f32 = lambda t: t.detach().float().cpu().numpy()
     X, Wr = f32(inp.X), f32(inp.Wr)
     bias = None if inp.bias is None else f32(inp.bias)
-    Wg, Wu, Wd = f32(inp.Wg), f32(inp.Wu), f32(inp.Wd)
+    scales = None
+    if cfg.fp8_weights:   # the oracle decodes the e4m3 codes itself and applies the row scales
+        dec = lambda q: orc.fp8e4m3_decode(q.cpu().numpy())
+        Wg, Wu, Wd = dec(inp.Wg), dec(inp.Wu), dec(inp.Wd)
+        scales = (f32(inp.Sg), f32(inp.Su), f32(inp.Sd))
+    else:
+        Wg, Wu, Wd = f32(inp.Wg), f32(inp.Wu), f32(inp.Wd)
     t0 = time.perf_counter()
     L = orc.router_logits(X, Wr, bias)
     idx, alpha = orc.topk(L, cfg.k, cfg.n_shared, cfg.renorm)
@@ -215,13 +233,13 @@ def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
     t_route = time.perf_counter() - t0
     probe = min(cfg.T, 16)
     t1 = time.perf_counter()
-    orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, None, tokens=np.arange(probe))
+    orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, None, tokens=np.arange(probe), scales=scales)
     per_tok = (time.perf_counter() - t1) / probe
     n = int(min(cfg.T, max(probe, target_s / max(per_tok, 1e-9))))
     rng = np.random.default_rng(5)
     toks = np.sort(rng.choice(cfg.T, size=n, replace=False))
     t2 = time.perf_counter()
-    orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, None, tokens=toks)
+    orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, None, tokens=toks, scales=scales)
     t_ffn = time.perf_counter() - t2
     t_layer = t_route + t_ffn * cfg.T / n
     return {"value": round(cfg.T / t_layer, 3), "unit": "tokens/s", "cores": orc.threads(),
@@ -267,7 +285,7 @@ def run_paged(args, cfg):
     experts_copied = sum((G if ld["early"] else int((counts[ld["group"] * G:(ld["group"] + 1) * G] > 0).sum()))
                          for ld in loads)
     n_exec = sum(1 for r in routed if r > 0)
-    expert_bytes = 3 * cfg.d * cfg.f * 2
+    expert_bytes = expert_slice_bytes(cfg)
     K = args.steps
     kernels = ["router", "topk", "route_count", "route_place", "gate_up", "down", "combine"]
     cap = K * (n_exec + len(loads) + 2)
@@ -435,7 +453,7 @@ def bench_stack(args, cfg, n_layers: int = 32) -> int:
         "per_layer_ms": round(stack_ms / n_layers, 4),
         "stack_ms": round(stack_ms, 3),
         "pct_bf16_peak": round(100.0 * flops / (stack_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "resident_expert_gb": round(n_layers * cfg.n_exp * 3 * cfg.d * cfg.f * 2 / 1e9, 1),
+        "resident_expert_gb": round(n_layers * cfg.n_exp * expert_slice_bytes(cfg) / 1e9, 1),
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -554,7 +572,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights; random-init, no checkpoint)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "T": cfg.T, "d": cfg.d, "E": cfg.E,
                    "k": cfg.k, "n_shared": cfg.n_shared, "f": cfg.f, "slots": layer.shape.P,
