@@ -705,9 +705,14 @@ hipError_t launch_mfma_lds(const GemmArgs &a, int max_rows, hipStream_t st)
     // never more than there can be tiles
     const unsigned g = std::min<unsigned>(grid_bound(a, max_rows, BM, BN), (unsigned)device_cus());
     if (g == 0) return hipSuccess;
+// fp8 B stages are half the size, so a deeper ring would fit; 5 and 6 stages
+// measured no faster than the bf16 kernel's 4 (OLMoE T=4096, Mixtral T=256).
+#ifndef MOE_FP8_STAGES
+#define MOE_FP8_STAGES NS
+#endif
     if (a.bfp8)
-        hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, true>), dim3(g), dim3(WM * WN * 64), 0,
-                           st, a);
+        hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, MOE_FP8_STAGES, WM, WN, GATEUP, true>), dim3(g),
+                           dim3(WM * WN * 64), 0, st, a);
     else
         hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, false>), dim3(g), dim3(WM * WN * 64), 0,
                            st, a);
