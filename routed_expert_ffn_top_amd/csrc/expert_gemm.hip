@@ -209,6 +209,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // B rows then take 32 bytes per stage; each wave's fragments are converted to
 // bf16 (exactly: every e4m3 value is a bf16 value) just before its MFMAs, and
 // the row scales multiply the fp32 accumulators in the epilogue.
+#ifndef MOE_GEMM_MAX_SLOTS
+#define MOE_GEMM_MAX_SLOTS kMaxExp
+#endif
+constexpr int kGemmMaxSlots = MOE_GEMM_MAX_SLOTS;
+
 template <int BM, int BN, int NS, int WM, int WN, bool GATEUP, bool BF8>
 __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
 {
@@ -229,8 +234,8 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     __shared__ int32_t s_route[2][GATEUP ? 1 : BM];   // by tile parity
     __shared__ float s_alpha[2][GATEUP ? 1 : BM];
     __shared__ float s_scale[2][BF8 ? BN : 1];          // row scales of the tile's B rows, by parity
-    __shared__ int32_t s_tpref[kMaxExp + 1];           // first logical tile of each slot
-    __shared__ int32_t s_off[kMaxExp + 1];
+    __shared__ int32_t s_tpref[kGemmMaxSlots + 1];     // first logical tile of each slot
+    __shared__ int32_t s_off[kGemmMaxSlots + 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -698,20 +703,30 @@ inline int device_cus()
     return cus;
 }
 
+// fp8 B stages are half the size, so a deeper ring would fit; 5 and 6 stages
+// measured no faster than the bf16 kernel's 4 (OLMoE T=4096, Mixtral T=256).
+#ifdef MOE_FP8_STAGES
+#define MOE_FP8_STAGES_OF(NS) MOE_FP8_STAGES
+#else
+#define MOE_FP8_STAGES_OF(NS) NS
+#endif
+
 template <int BM, int BN, int NS, int WM, int WN, bool GATEUP>
 hipError_t launch_mfma_lds(const GemmArgs &a, int max_rows, hipStream_t st)
 {
-    // one persistent workgroup per compute unit (the LDS ring fills one CU),
-    // never more than there can be tiles
-    const unsigned g = std::min<unsigned>(grid_bound(a, max_rows, BM, BN), (unsigned)device_cus());
+    // persistent workgroups, as many as fit on the GPU at once (one per
+    // compute unit when the LDS ring fills it), never more than there can be
+    // tiles
+    if (a.P > kGemmMaxSlots) return hipErrorInvalidValue;   // the slot tables live in LDS
+    auto kern = a.bfp8 ? (const void *)k_gemm_mfma_lds<BM, BN, MOE_FP8_STAGES_OF(NS), WM, WN, GATEUP, true>
+                       : (const void *)k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, false>;
+    int per_cu = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WM * WN * 64, 0) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const unsigned g = std::min<unsigned>(grid_bound(a, max_rows, BM, BN), (unsigned)per_cu * (unsigned)device_cus());
     if (g == 0) return hipSuccess;
-// fp8 B stages are half the size, so a deeper ring would fit; 5 and 6 stages
-// measured no faster than the bf16 kernel's 4 (OLMoE T=4096, Mixtral T=256).
-#ifndef MOE_FP8_STAGES
-#define MOE_FP8_STAGES NS
-#endif
     if (a.bfp8)
-        hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, MOE_FP8_STAGES, WM, WN, GATEUP, true>), dim3(g),
+        hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, MOE_FP8_STAGES_OF(NS), WM, WN, GATEUP, true>), dim3(g),
                            dim3(WM * WN * 64), 0, st, a);
     else
         hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, false>), dim3(g), dim3(WM * WN * 64), 0,
@@ -736,6 +751,9 @@ hipError_t launch_simple(const GemmArgs &a, int max_rows, hipStream_t st)
 #ifndef MOE_RING_TILE
 #define MOE_RING_TILE 256, 256, 4, 4, 2
 #endif
+#ifndef MOE_DOWN_TILE
+#define MOE_DOWN_TILE MOE_RING_TILE
+#endif
 
 hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
                           hipStream_t st)
@@ -758,7 +776,7 @@ hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool
         if (a.bfp8) return hipErrorInvalidValue;
         return launch_simple<uint16_t, false>(a, max_rows, st);
     }
-    return launch_mfma_lds<MOE_RING_TILE, false>(a, max_rows, st);
+    return launch_mfma_lds<MOE_DOWN_TILE, false>(a, max_rows, st);
 }
 
 }  // namespace moe
