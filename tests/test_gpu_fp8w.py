@@ -105,3 +105,28 @@ def test_fp8w_quantisation_error_is_small():
     d = rel_err(f8, fb.astype(np.float64))
     say(f"  rel diff fp8 vs bf16 weights: {d:.3e}")
     assert d < 0.1
+
+
+def test_fp8w_edge_shapes():
+    say("fp8 weights: one token and a ragged token count")
+    for T in (1, 77):
+        _check_layer(MID8.with_(T=T, name=f"mid_fp8w_T{T}"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "bf16_fp8w"])
+def test_device_pack_equals_host_pack(dtype):
+    say(f"gate/up packing on the device equals the host packing ({dtype})")
+    cfg = MID.with_(dtype=dtype, E=3, k=2, T=4)
+    inp = gpu_inputs(cfg)
+    s = B.make_shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, P=cfg.E, dtype=dtype)
+    arena = B.Arena(s)
+    scales = (inp.Sg, inp.Su, inp.Sd) if cfg.fp8_weights else None
+    for e in range(cfg.E):
+        g, u, _ = B.expert_slices(inp.Wg, inp.Wu, inp.Wd, scales, e)
+        dev = torch.empty_like(arena.plane_gu[0])
+        B.moe_pack_gate_up(s, g, u, dev, 1, 0, 0)
+        host = torch.empty_like(dev, device="cpu")
+        B.moe_pack_gate_up_host(s, g.cpu(), u.cpu(), host)
+        torch.cuda.synchronize()
+        assert torch.equal(dev.cpu().view(torch.uint8), host.view(torch.uint8)), f"expert {e}"
+    arena.close()
