@@ -11,9 +11,11 @@
  * Every function computes its result from the definition, with no blocking,
  * fusion or reordering:
  *   oracle_router_logits  L = X W_r (+ bias), fp32, one fused multiply-add
- *                         per term in ascending hidden index.  The top-k
- *                         decision is taken on these fp32 values, so the order
- *                         of the chain is part of the contract.
+ *                         per term: 16 partial chains over interleaved runs
+ *                         of 8 hidden indices, each in ascending index order,
+ *                         then added in ascending chain order.  The top-k
+ *                         decision is taken on these fp32 values, so this
+ *                         order is part of the contract.
  *   oracle_topk           top-k of E experts per token (section 2.2: "a router
  *                         assigns each token to the top-k of E experts"), ties
  *                         to the lower expert id; softmax weights in fp64,
@@ -62,9 +64,13 @@ void oracle_set_threads(int n)
 }
 
 /*
- * Router logits. L[t][e] = sum over i = 0..d-1 of X[t][i] * Wr[i][e], evaluated
- * as acc = fmaf(X[t][i], Wr[i][e], acc) for ascending i from acc = 0.0f, then
- * L = acc + bias[e] (one fp32 addition) when a bias is given.
+ * Router logits. L[t][e] = sum over i = 0..d-1 of X[t][i] * Wr[i][e] in fp32,
+ * evaluated in one fixed order. The hidden index is cut into runs of 8
+ * consecutive values; run r = i / 8 feeds partial sum c = r mod 16. Each
+ * partial sum is one fused multiply-add chain p[c] = fmaf(X[t][i], Wr[i][e],
+ * p[c]) over its indices in ascending order, from p[c] = 0.0f. The 16 partial
+ * sums are then added left to right, s = ((p[0] + p[1]) + p[2]) + ... + p[15],
+ * and L = s + bias[e] (one fp32 addition) when a bias is given.
  * X: [T][ldx] fp32 values (bf16 inputs widened exactly), Wr: [d][E], bias: [E]
  * or NULL, L: [T][E].
  */
@@ -76,11 +82,16 @@ void oracle_router_logits(int64_t T, int64_t d, int64_t E, const float *X,
 #pragma omp parallel for schedule(static)
     for (t = 0; t < T; ++t) {
         for (int64_t e = 0; e < E; ++e) {
-            float acc = 0.0f;
-            for (int64_t i = 0; i < d; ++i)
-                acc = fmaf(X[t * ldx + i], Wr[i * E + e], acc);
-            if (bias) acc = acc + bias[e];
-            L[t * E + e] = acc;
+            float p[16];
+            for (int c = 0; c < 16; ++c) p[c] = 0.0f;
+            for (int64_t i = 0; i < d; ++i) {
+                const int c = (int)((i >> 3) & 15);
+                p[c] = fmaf(X[t * ldx + i], Wr[i * E + e], p[c]);
+            }
+            float s = p[0];
+            for (int c = 1; c < 16; ++c) s = s + p[c];
+            if (bias) s = s + bias[e];
+            L[t * E + e] = s;
         }
     }
 }

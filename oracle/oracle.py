@@ -50,6 +50,8 @@ class Oracle:
             if path != LIB:
                 raise FileNotFoundError(path)
             build()
+        elif path == LIB and os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()   # the default build is older than its source
         self.path = path
         lib = ctypes.CDLL(path)
         lib.oracle_router_logits.argtypes = [_i64, _i64, _i64, _ptr, _i64, _ptr, _ptr, _ptr]

@@ -117,17 +117,21 @@ def check_router_exact_integers(orc):
 
 
 def check_router_error_bound(orc):
-    """|L - exact| <= gamma_d * sum|x w| + |bias rounding| (recursive sum)."""
+    """|L - exact| <= gamma_n * sum|x w| with n = m + 15: each of the 16
+    partial chains holds at most m = 8 * ceil(d / 128) terms and the partial
+    sums take 15 more additions (Higham's bound for recursive summation, with
+    fused products rounded once)."""
     rng = _rng(12)
-    T, d, E = 9, 2048, 64
-    X = _bf16_values(rng.standard_normal((T, d), dtype=np.float32))
-    Wr = rng.standard_normal((d, E), dtype=np.float32) * np.float32(0.02)
-    L = orc.router_logits(X, Wr, None).astype(np.float64)
-    exact = X.astype(np.float64) @ Wr.astype(np.float64)
     u = 2.0 ** -24
-    gamma = d * u / (1 - d * u)
-    bound = gamma * (np.abs(X.astype(np.float64)) @ np.abs(Wr.astype(np.float64)))
-    assert np.all(np.abs(L - exact) <= bound)
+    for T, d, E in ((9, 2048, 64), (5, 320, 8)):
+        X = _bf16_values(rng.standard_normal((T, d), dtype=np.float32))
+        Wr = rng.standard_normal((d, E), dtype=np.float32) * np.float32(0.02)
+        L = orc.router_logits(X, Wr, None).astype(np.float64)
+        exact = X.astype(np.float64) @ Wr.astype(np.float64)
+        n = 8 * ((d + 127) // 128) + 15
+        gamma = n * u / (1 - n * u)
+        bound = gamma * (np.abs(X.astype(np.float64)) @ np.abs(Wr.astype(np.float64)))
+        assert np.all(np.abs(L - exact) <= bound)
 
 
 # ----------------------------------------------------------------- top-k --
