@@ -184,11 +184,14 @@ moe_status moe_device_errors(const moe_shape *shape, void *ws, size_t ws_bytes,
  *          hidden index: the layout of a linear layer's weight d -> E)
  *   bias   device [E] fp32 or NULL (added after the product)
  *   logits device [T][E] fp32, output
- * Requires X 16-byte aligned, W_r 4-byte aligned, and for fp32 X
- * ldx % 4 == 0 (bf16 X already needs ldx % 8 == 0).
- * logits[t][e] = acc + bias[e], where acc is the fp32 fused multiply-add
- * chain over i = 0..d-1 in ascending order starting from 0: this fixes the
- * bits of every logit, so the top-k decision is reproducible.
+ * Requires X and W_r 16-byte aligned, and for fp32 X ldx % 4 == 0 (bf16 X
+ * already needs ldx % 8 == 0; d % 4 == 0 holds for every shape).
+ * logits[t][e] = s + bias[e], where s is the fp32 dot product of X[t] and
+ * W_r[e] with each term one fused multiply-add, in this order: the hidden
+ * index is cut into runs of 8 consecutive values, run r = i / 8 feeds partial
+ * sum r % 16, each partial sum is a chain in ascending i starting from 0, and
+ * s = ((p0 + p1) + p2) + ... + p15. This fixes the bits of every logit, so
+ * the top-k decision is reproducible.
  */
 moe_status moe_router_logits(const moe_shape *shape, const void *X,
                              const float *W_r, const float *bias,

@@ -130,11 +130,11 @@ moe_status check_phi(const moe_shape *s, const int32_t *phi, PhiArg *out)
 template <typename T>
 T *ws_at(void *ws, size_t off) { return (T *)((char *)ws + off); }
 
-// The router reads X rows in 16-byte pieces.
+// The router reads X and W_r rows in 16-byte pieces.
 moe_status check_router_args(const moe_shape *s, const void *X, const float *W_r)
 {
-    if (!aligned(X, 16) || !aligned(W_r, 4))
-        return fail(MOE_ERR_INVALID_ARG, "router: X must be 16-byte and W_r 4-byte aligned");
+    if (!aligned(X, 16) || !aligned(W_r, 16))
+        return fail(MOE_ERR_INVALID_ARG, "router: X and W_r must be 16-byte aligned");
     if (s->dtype == MOE_DT_F32 && (s->ldx % 4) != 0)
         return fail(MOE_ERR_UNSUPPORTED, "router: fp32 X needs ldx %% 4 == 0");
     return MOE_OK;

@@ -2,10 +2,11 @@
 // each token to the top-k of E experts; the per-route weight alpha scales the
 // expert output in Eq. 2).
 //
-// Router: L[t][e] = fp32 fused multiply-add chain over the hidden index in
-// ascending order, then + bias[e]. The chain is not split or reassociated:
-// the top-k decision is taken on these bits, so they must be reproducible.
-// A lane owns one token and a few experts; W_r comes through scalar loads.
+// Router: L[t][e] = sum over the hidden index of x * w in fp32, each term one
+// fused multiply-add, in a fixed order: runs of 8 consecutive hidden indices,
+// run r feeding partial sum r mod 16, each partial sum ascending in the index
+// from 0, the 16 partial sums added in ascending order, then + bias[e]. The
+// top-k decision is taken on these bits, so the order is part of the result.
 //
 // Top-k: one wave64 per token; each lane owns experts lane, lane+64, ...
 // An expert's rank is the number of experts with a larger logit plus the
@@ -17,257 +18,227 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h)
-{
-    return __uint_as_float(((uint32_t)h) << 16);
-}
-
-template <typename TX>
-__device__ __forceinline__ float load_x(const TX *p);
-template <>
-__device__ __forceinline__ float load_x<float>(const float *p) { return *p; }
-template <>
-__device__ __forceinline__ float load_x<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
-
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// For each expert j < NE: acc[j] += bcast(w[j], q) * x[q] for q = 0..15 in
-// ascending order, where bcast(w, q) is the value that lane q of each 16-lane
-// row holds (DPP row_newbcast:q): the 16 lanes of a row hold 16 consecutive
-// weights of one expert. The NE chains are interleaved (q outer, j inner) so
-// that consecutive multiply-adds are independent. One s_nop 1 covers the two
-// wait states a DPP source needs after a vector ALU write.
-template <int NE>
-__device__ __forceinline__ void fmac16_bcast(float *acc, const float *w, const float *x);
-
-template <>
-__device__ __forceinline__ void fmac16_bcast<1>(float *acc, const float *w, const float *x)
+// Workgroup barrier that publishes this wave's LDS writes (lgkmcnt(0)) but
+// leaves its global loads in flight; __syncthreads would also drain those.
+// gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] at bits 15:14.
+__device__ __forceinline__ void lds_barrier()
 {
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_fmac_f32_dpp %0, %1, %2 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %3 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %4 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %7 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %8 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %9 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %10 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %11 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %12 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %13 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %14 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %15 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %1, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf"
-        : "+v"(acc[0])
-        : "v"(w[0]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_s_barrier();
 }
 
-template <>
-__device__ __forceinline__ void fmac16_bcast<2>(float *acc, const float *w, const float *x)
+// Router logits on the fp32 matrix cores. v_mfma_f32_4x4x1_16b performs 16
+// independent 4 x 4 outer-product updates D_b += A_b B_b^T: lane l supplies
+// A_b[l % 4] and B_b[l % 4] of block b = l / 4 and holds D_b[r][l % 4] in its
+// register r. Each update is one fused multiply-add per element, so every
+// accumulator element is an fmaf chain (checked bit for bit against fmaf,
+// signed zeros and denormals included).
+//
+// Block b is partial sum b of the logit. At step s (0..7) of hidden group g
+// (128 indices), lane l works on hidden index (16 g + b) * 8 + s: run 16 g + b
+// of 8 consecutive indices, which feeds partial sum (16 g + b) mod 16 = b, and
+// within a run the indices ascend. Rows of a block are 4 tokens, columns 4
+// experts.
+//
+// A wave owns TQ token quads x 4 expert quads (4 TQ tokens x 16 experts, 4 TQ
+// independent accumulators, so consecutive instructions do not wait on each
+// other); the 4 waves of a workgroup take 4 consecutive token blocks of the
+// same 16 experts (grid: ceil(T / (16 TQ)) x ceil(E / 16)).
+//   x: each lane loads its run of each of its token rows (8 values) into a
+//      register ring PF groups deep; the 16 lanes that share a row read 16
+//      adjacent runs, so every load reads whole contiguous row segments.
+//   W_r: the 16 expert rows of a group (8 KB) are shared by the 4 waves
+//      through a ring of NB LDS buffers. Each wave fetches a quarter of group
+//      g + 2 into registers and writes its quarter of group g + 1 into LDS
+//      while it multiplies group g; one barrier per group publishes the
+//      writes and frees the buffer the next writes take.
+// The loads of a group are spread between the multiplies of the previous one
+// so that the matrix pipe keeps busy while they queue.
+//
+// Hidden indices at or past d are taken as x = -0 and w = +0: the product is
+// -0, and a + (-0) = a for every a, +0 and -0 included, so padded steps leave
+// the chains unchanged. Token and expert rows past T and E are clamped to the
+// last row and their results dropped. At the end the 16 partial sums of each
+// (token, expert) pass through LDS and are added in ascending order, then the
+// bias.
+template <typename TX, int TQ, bool FULL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_router_logits(
+    const TX *__restrict__ X, int64_t ldx, const float *__restrict__ Wr, const float *__restrict__ bias,
+    float *__restrict__ L, int T, int d, int E)
 {
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_fmac_f32_dpp %0, %2, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %6 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %7 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %8 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %9 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %10 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %11 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %12 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %12 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %13 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %13 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %14 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %14 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %15 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %15 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %18 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %18 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %2, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %3, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf"
-        : "+v"(acc[0]), "+v"(acc[1])
-        : "v"(w[0]), "v"(w[1]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
-}
+    constexpr int XV = sizeof(TX) == 2 ? 1 : 2;   // 16-byte pieces per run of 8 x values
+    constexpr int XE = 16 / sizeof(TX);            // x values per piece
+#ifdef MOE_ROUTER_PF
+    constexpr int PF = MOE_ROUTER_PF;
+#else
+    constexpr int PF = TQ == 1 ? 4 : 3;            // x ring depth in groups (measured best)
+#endif
+    constexpr int NB = 3;                          // W_r ring depth in groups (LDS)
+    constexpr int U = PF * 2;                      // main-loop unroll: a multiple of PF and of 2
+    constexpr int RS = 64 * TQ + 4;                // LDS stride of one partial sum (bank spread)
+    constexpr uint32_t XPAD = sizeof(TX) == 2 ? 0x80008000u : 0x80000000u;   // -0 in every x slot
+    __shared__ u32x4_t wbuf[NB][512];              // 16 expert rows x 16 runs x 2 halves of 16 bytes
+    __shared__ float red[4][16 * RS];
 
-template <>
-__device__ __forceinline__ void fmac16_bcast<4>(float *acc, const float *w, const float *x)
-{
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %5, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %7, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf"
-        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
-        : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
-}
-
-// Router logits. A wave owns 64 tokens (one per lane) and NE consecutive
-// experts; the 4 waves of a workgroup take 4 expert blocks of the same 64
-// tokens (grid: T/64 x ceil(E / (4 NE))). W_r is [E][d]. The hidden index is
-// walked in 16-wide blocks: lane l loads weight (l % 16) of the block for each
-// of its experts (one coalesced 64-byte read per expert) and its own token's
-// 16 x values; a lane converts each x value once and uses it for NE chains,
-// with the weight broadcast across the row inside the multiply-add (see
-// fmac16_bcast). Loads run PF blocks ahead of the arithmetic.
-template <typename TX, int NE>
-__global__ __launch_bounds__(256) void k_router_logits(const TX *__restrict__ X, int64_t ldx,
-                                                       const float *__restrict__ Wr,
-                                                       const float *__restrict__ bias,
-                                                       float *__restrict__ L, int T, int d, int E)
-{
-    constexpr int PF = sizeof(TX) == 2 ? 8 : 4;
-    constexpr int XV = sizeof(TX) == 2 ? 2 : 4;   // 16-byte loads per 16 x values
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int eb = (blockIdx.y * 4 + wave) * NE;   // first expert of this wave
-    if (eb >= E) return;                           // no barriers below
-    const int t = blockIdx.x * 64 + lane;
-    const TX *xrow = X + (int64_t)min(t, T - 1) * ldx;
-    const float *wsrc[NE];
-#pragma unroll
-    for (int j = 0; j < NE; ++j) wsrc[j] = Wr + (int64_t)min(eb + j, E - 1) * d + (lane & 15);
+    const int wave = threadIdx.x >> 6;
+    const int b = lane >> 2, q = lane & 3;
+    const int t0 = (blockIdx.x * 4 + wave) * (4 * TQ);
+    const int e0 = blockIdx.y * 16;
+    const int ng = (d + 127) >> 7;
 
-    float acc[NE];
+    // LDS slot of (expert row r, run b, half h) of a group: row-major, the 32
+    // pieces of a row rotated by rot(r % 4) = 8 (r & 1) + (r & 2) / 2, so that
+    // the 16 lanes of a read (runs b0..b0+3 of rows 4v..4v+3, one half) hit 16
+    // distinct 16-byte bank groups.
+    auto rot = [](int r) { return 8 * (r & 1) + ((r >> 1) & 1); };
+    int rslot[4][2];
 #pragma unroll
-    for (int j = 0; j < NE; ++j) acc[j] = 0.0f;
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) rslot[v][h] = (4 * v + q) * 32 + ((2 * b + h + rot(q)) & 31);
+    // this lane's two pieces of every group: slot S = (2 wave + k) * 64 + lane
+    const float *wsrc[2];
+    int wslot[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int S = (2 * wave + k) * 64 + lane, r = S >> 5;
+        const int p = ((S & 31) - rot(r)) & 31;   // 2 * run + half
+        wslot[k] = S;
+        wsrc[k] = Wr + (int64_t)min(e0 + r, E - 1) * d + (p >> 1) * 8 + (p & 1) * 4;
+    }
 
-    const int nb = d >> 4;   // whole 16-wide blocks
-    auto load = [&](int b, u32x4_t *xv, float *wv) {
-        const int i0 = min(b, nb - 1) * 16;   // past the end: re-read the last block
+    const TX *xrow[TQ];
 #pragma unroll
-        for (int h = 0; h < XV; ++h) xv[h] = *(const u32x4_t *)((const char *)(xrow + i0) + 16 * h);
-#pragma unroll
-        for (int j = 0; j < NE; ++j) wv[j] = wsrc[j][i0];
-    };
-    auto compute = [&](const u32x4_t *xv, const float *wv) {
-        float x[16];
-        if (sizeof(TX) == 2) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t v = xv[q / 4][q % 4];
-                x[2 * q] = __uint_as_float(v << 16);
-                x[2 * q + 1] = __uint_as_float(v & 0xffff0000u);
-            }
+    for (int u = 0; u < TQ; ++u) xrow[u] = X + (int64_t)min(t0 + 4 * u + q, T - 1) * ldx;
+
+    // Loads of group g are clamped to the last group (a re-read whose values
+    // are not used). With FULL (d % 128 == 0) every run is inside the row;
+    // else a piece at or past d is read from the row start (x: replaced by
+    // the pad here; w: masked where it is read), so no load depends on a
+    // branch.
+    auto load_x = [&](int g, int j, u32x4_t (&xv)[TQ][XV]) {
+        const int u = j / XV, h = j % XV;
+        const int i = min(g, ng - 1) * 128 + b * 8 + h * XE;
+        if (FULL) {
+            xv[u][h] = *(const u32x4_t *)(xrow[u] + i);
         } else {
+            const bool in = i < d;
+            const u32x4_t v = *(const u32x4_t *)(xrow[u] + (in ? i : 0));
 #pragma unroll
-            for (int q = 0; q < 16; ++q) x[q] = __uint_as_float(xv[q / 4][q % 4]);
+            for (int c = 0; c < 4; ++c) xv[u][h][c] = in ? v[c] : XPAD;
         }
-        fmac16_bcast<NE>(acc, wv, x);
     };
-    if (nb > 0) {
-        u32x4_t xr[PF][XV];
-        float wr[PF][NE];
-#pragma unroll
-        for (int u = 0; u < PF; ++u) load(u, xr[u], wr[u]);
-        int b0 = 0;
-        for (; b0 + PF <= nb; b0 += PF) {
-#pragma unroll
-            for (int u = 0; u < PF; ++u) {
-                u32x4_t xc[XV];
-                float wc[NE];
-#pragma unroll
-                for (int h = 0; h < XV; ++h) xc[h] = xr[u][h];
-#pragma unroll
-                for (int j = 0; j < NE; ++j) wc[j] = wr[u][j];
-                load(b0 + u + PF, xr[u], wr[u]);
-                compute(xc, wc);
-            }
+    auto load_w = [&](int g, int k, u32x4_t (&wt)[2]) {
+        const int i = min(g, ng - 1) * 128;
+        if (FULL) {
+            wt[k] = *(const u32x4_t *)(wsrc[k] + i);
+        } else {
+            const int off = (int)(wsrc[k] - Wr) % d;   // hidden index of the piece in its row
+            wt[k] = *(const u32x4_t *)(wsrc[k] + (i + off < d ? i : -off));
         }
-        // the last nb - b0 < PF blocks are in the ring, block b0 + u in slot u
+    };
+    auto read_w = [&](int g, u32x4_t (&wv)[4][2]) {
+        const u32x4_t *buf = wbuf[g % NB];
 #pragma unroll
-        for (int u = 0; u < PF - 1; ++u)
-            if (b0 + u < nb) compute(xr[u], wr[u]);
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                wv[v][h] = buf[rslot[v][h]];
+                if (!FULL && g * 128 + b * 8 + h * 4 >= d) wv[v][h] = u32x4_t{0, 0, 0, 0};
+            }
+    };
+
+    f32x4_t acc[TQ][4];
+#pragma unroll
+    for (int u = 0; u < TQ; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // One group: 8 hidden steps x 4 TQ blocks x 4 expert quads of multiplies.
+    // Spread between them: the x loads of group g + PF - 1 into the x slot
+    // that group g - 1 released, the W_r loads of group g + 2 into wn, and the
+    // LDS writes of group g + 1 from wp. LOADS = false: none of these.
+    constexpr int NX = TQ * XV;
+    auto group = [&](int g, const u32x4_t (&xv)[TQ][XV], u32x4_t (&xn)[TQ][XV], u32x4_t (&wn)[2],
+                     const u32x4_t (&wp)[2], bool loads) {
+        lds_barrier();   // group g's rows are in LDS; the buffer of group g + 1 - NB is free
+        u32x4_t wv[4][2];
+        read_w(g, wv);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            float a[TQ];
+#pragma unroll
+            for (int u = 0; u < TQ; ++u) {
+                if (sizeof(TX) == 2) {
+                    const uint32_t w2 = xv[u][0][s >> 1];
+                    a[u] = __uint_as_float((s & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+                } else {
+                    a[u] = __uint_as_float(xv[u][s >> 2][s & 3]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < TQ; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[u][v] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[u], __uint_as_float(wv[v][s >> 2][s & 3]),
+                                                                  acc[u][v], 0, 0, 0);
+            if (loads) {
+#pragma unroll
+                for (int j = s * NX / 8; j < (s + 1) * NX / 8; ++j) load_x(g + PF - 1, j, xn);
+                if (s == 1 || s == 5) load_w(g + 2, s >> 2, wn);
+                if (s == 3 || s == 7) wbuf[(g + 1) % NB][wslot[s >> 2]] = wp[s >> 2];
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep this step's loads between its multiplies and the next step's
+        }
+    };
+
+    // prologue: x groups 0 .. PF-2 into x slots; W_r group 0 into LDS, group 1 into registers
+    u32x4_t xr[PF][TQ][XV], wt[2][2];
+#pragma unroll
+    for (int u = 0; u < PF - 1; ++u)
+#pragma unroll
+        for (int j = 0; j < NX; ++j) load_x(u, j, xr[u]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) load_w(0, k, wt[0]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) load_w(1, k, wt[1]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) wbuf[0][wslot[k]] = wt[0][k];
+
+    // x slot g % PF holds group g; W_r registers wt[g % 2] hold group g + 1
+    // (written to LDS during group g) and then take group g + 2.
+    int g0 = 0;
+    for (; g0 + U <= ng; g0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            group(g0 + u, xr[u % PF], xr[(u + PF - 1) % PF], wt[u % 2], wt[(u + 1) % 2], true);
     }
-    // hidden indices past the last whole block, in order
-    for (int i = nb * 16; i < d; ++i) {
-        const float xv = load_x<TX>(xrow + i);
 #pragma unroll
-        for (int j = 0; j < NE; ++j)
-            acc[j] = __builtin_fmaf(xv, Wr[(int64_t)min(eb + j, E - 1) * d + i], acc[j]);
-    }
-    if (t < T) {
+    for (int u = 0; u < U - 1; ++u)
+        if (g0 + u < ng) group(g0 + u, xr[u % PF], xr[(u + PF - 1) % PF], wt[u % 2], wt[(u + 1) % 2], true);
+
+    // partial sum b of (token 4u + r, expert 4v + q) -> red[b][(4u + r) * 16 + 4v + q]
+    float *rw = red[wave];
 #pragma unroll
-        for (int j = 0; j < NE; ++j)
-            if (eb + j < E) L[(int64_t)t * E + eb + j] = bias ? acc[j] + bias[eb + j] : acc[j];
+    for (int u = 0; u < TQ; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rw[b * RS + (4 * u + r) * 16 + 4 * v + q] = acc[u][v][r];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) {
+        const int o = lane + 64 * j;
+        const int t = t0 + (o >> 4), e = e0 + (o & 15);
+        float s = rw[o];
+#pragma unroll
+        for (int c = 1; c < 16; ++c) s = s + rw[c * RS + o];
+        if (t < T && e < E) L[(int64_t)t * E + e] = bias ? s + bias[e] : s;
     }
 }
 
@@ -378,13 +349,17 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ L, int E
 
 }  // namespace
 
-template <typename TX, int NE>
+template <typename TX, int TQ>
 hipError_t launch_router_t(const moe_shape &s, const void *X, const float *Wr, const float *bias, float *L,
                            hipStream_t st)
 {
-    const dim3 grid((s.T + 63) / 64, (s.E + 4 * NE - 1) / (4 * NE));
-    hipLaunchKernelGGL((k_router_logits<TX, NE>), grid, dim3(256), 0, st, (const TX *)X, s.ldx, Wr, bias, L,
-                       s.T, s.d, s.E);
+    const dim3 grid((s.T + 16 * TQ - 1) / (16 * TQ), (s.E + 15) / 16);
+    if (s.d % 128 == 0)
+        hipLaunchKernelGGL((k_router_logits<TX, TQ, true>), grid, dim3(256), 0, st, (const TX *)X, s.ldx, Wr, bias,
+                           L, s.T, s.d, s.E);
+    else
+        hipLaunchKernelGGL((k_router_logits<TX, TQ, false>), grid, dim3(256), 0, st, (const TX *)X, s.ldx, Wr, bias,
+                           L, s.T, s.d, s.E);
     return hipGetLastError();
 }
 
@@ -392,19 +367,20 @@ hipError_t launch_router_logits(const moe_shape &s, const void *X, const float *
                                 const float *bias, float *L, hipStream_t st)
 {
     if (s.T == 0) return hipSuccess;
-    // experts per wave: 4 while that still gives every SIMD a wave, else fewer
-    const int64_t tg = (s.T + 63) / 64;
-    int ne = tg * ((s.E + 15) / 16) >= 256 ? 4 : (tg * ((s.E + 7) / 8) >= 256 ? 2 : 1);
-#ifdef MOE_ROUTER_NE
-    ne = MOE_ROUTER_NE;
+    // token quads per wave: 4 (16 accumulators) while that still gives every
+    // SIMD a wave, else fewer accumulators and more waves
+    const int64_t eb = (s.E + 15) / 16;
+    int tq = ((s.T + 15) / 16) * eb >= 1024 ? 4 : (((s.T + 7) / 8) * eb >= 1024 ? 2 : 1);
+#ifdef MOE_ROUTER_TQ
+    tq = MOE_ROUTER_TQ;
 #endif
     if (act_bf16(s)) {
-        if (ne == 4) return launch_router_t<uint16_t, 4>(s, X, Wr, bias, L, st);
-        if (ne == 2) return launch_router_t<uint16_t, 2>(s, X, Wr, bias, L, st);
+        if (tq == 4) return launch_router_t<uint16_t, 4>(s, X, Wr, bias, L, st);
+        if (tq == 2) return launch_router_t<uint16_t, 2>(s, X, Wr, bias, L, st);
         return launch_router_t<uint16_t, 1>(s, X, Wr, bias, L, st);
     }
-    if (ne == 4) return launch_router_t<float, 4>(s, X, Wr, bias, L, st);
-    if (ne == 2) return launch_router_t<float, 2>(s, X, Wr, bias, L, st);
+    if (tq == 4) return launch_router_t<float, 4>(s, X, Wr, bias, L, st);
+    if (tq == 2) return launch_router_t<float, 2>(s, X, Wr, bias, L, st);
     return launch_router_t<float, 1>(s, X, Wr, bias, L, st);
 }
 
