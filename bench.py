@@ -140,6 +140,90 @@ def summarize_pmc(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, out, c
     print(open(out).read())
 
 
+def _stats_avg_us(stats_csv) -> dict:
+    """Average duration (us) per kernel name from a rocprofv3 kernel_stats.csv."""
+    import csv
+    out = {}
+    for r in csv.DictReader(open(stats_csv)):
+        out[r.get("Name") or r.get("KernelName") or "?"] = float(r.get("AverageNs", 0)) / 1e3
+    return out
+
+
+# The layer's kernels, by a test on the full kernel name.
+LAYER_KERNELS = (
+    ("router", lambda k: "k_router_logits<" in k),
+    ("top-k", lambda k: "k_topk<" in k),
+    ("route count", lambda k: "k_route_count" in k),
+    ("route place", lambda k: "k_route_place" in k),
+    ("gate/up", lambda k: "k_gemm_mfma_lds<" in k and ", true, false>" in k),
+    ("down", lambda k: "k_gemm_mfma_lds<" in k and ", false, false>" in k),
+    ("combine", lambda k: "k_combine<" in k),
+)
+
+
+def layer_algorithmic(cfg) -> dict:
+    """Algorithmic HBM bytes and MFMA FLOPs per launch of each layer kernel
+    (bf16 activations and weights; the method's own traffic: each input read
+    once, each output written once)."""
+    T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f
+    kp = k + cfg.n_shared
+    R = T * kp
+    return {
+        "router": (T * d * 2 + E * d * 4 + T * E * 4, 2.0 * T * E * d),
+        "top-k": (T * E * 4 + T * kp * 8, 0.0),
+        "route count": (R * 4, 0.0),
+        "route place": (R * 4 + R * 12, 0.0),
+        "gate/up": (E * 2 * f * d * 2 + R * d * 2 + R * f * 2, 4.0 * R * d * f),
+        "down": (E * d * f * 2 + R * f * 2 + R * d * 4, 2.0 * R * d * f),
+        "combine": (R * d * 4 + 2 * T * d * 4, 0.0),
+    }
+
+
+def summarize_kernels(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, mfma_csv, stats_csv, out,
+                      command, workload) -> None:
+    """Per layer kernel: trace-average duration, HBM bytes (FETCH_SIZE and
+    WRITE_SIZE scaled by the 1 GiB copy calibration) and GB/s, algorithmic
+    bytes, MFMA busy % (MfmaUtil) and MFMA FLOPs counted by the hardware
+    (MfmaFlopsBF16 + MfmaFlopsF32) against the algorithmic FLOPs."""
+    from routed_expert_ffn_top_amd.inputs import CONFIGS
+    cfg = CONFIGS[workload]
+    fetch = _pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_csv, "WRITE_SIZE")
+    is_copy = lambda k: "elementwise" in k.lower() and "Mul" in k
+    cf = max(v for k, v in _pmc_per_kernel(calib_fetch_csv, "FETCH_SIZE").items() if is_copy(k))[0]
+    cw = max(v for k, v in _pmc_per_kernel(calib_write_csv, "WRITE_SIZE").items() if is_copy(k))[0]
+    kf, kw = float(1 << 30) / (cf * 1024.0), float(1 << 30) / (cw * 1024.0)
+    util = _pmc_per_kernel(mfma_csv, "MfmaUtil")
+    fl16 = _pmc_per_kernel(mfma_csv, "MfmaFlopsBF16")
+    fl32 = _pmc_per_kernel(mfma_csv, "MfmaFlopsF32")
+    dur = _stats_avg_us(stats_csv)
+    alg = layer_algorithmic(cfg)
+
+    def one(d, test):
+        hits = [v[0] for k, v in d.items() if test(k)]
+        return max(hits) if hits else float("nan")
+
+    with open(out, "w") as fh:
+        fh.write(f"# Layer kernels: HBM traffic, bandwidth and MFMA use ({workload}: T={cfg.T}, d={cfg.d}, "
+                 f"E={cfg.E}, k={cfg.k}, f={cfg.f})\n\n")
+        fh.write(f"Commands: {command}\n\n")
+        fh.write(f"HBM bytes = FETCH_SIZE x {kf:.3f} + WRITE_SIZE x {kw:.3f} (KiB per dispatch; the factors make a "
+                 "plain 1 GiB device copy read and write 1 GiB). Duration: trace average of the timed run. "
+                 "MFMA busy: MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs). MFMA FLOPs: "
+                 "(SQ_INSTS_VALU_MFMA_MOPS_BF16 + _F32) x 512, all rows of every tile included.\n\n")
+        fh.write("| kernel | avg us | HBM MB | HBM GB/s | algorithmic MB | HBM / algorithmic | MFMA busy % | "
+                 "MFMA GFLOP counted | algorithmic GFLOP |\n|---|---|---|---|---|---|---|---|---|\n")
+        for name, test in LAYER_KERNELS:
+            us = one({k: (v, 1) for k, v in dur.items()}, test)
+            hb = one(fetch, test) * 1024.0 * kf + one(write, test) * 1024.0 * kw
+            ab, af = alg[name]
+            u = one(util, test)
+            fc = one(fl16, test) + one(fl32, test)
+            fh.write(f"| {name} | {us:.1f} | {hb / 1e6:.1f} | {hb / (us * 1e-6) / 1e9:.0f} | {ab / 1e6:.1f} | "
+                     f"{hb / ab:.2f} | {u:.1f} | {fc / 1e9:.1f} | {af / 1e9:.1f} |\n")
+    print(open(out).read())
+
+
 def summarize_stats(stats_csv, out, command) -> None:
     """Markdown table of a rocprofv3 --stats kernel_stats.csv."""
     import csv
@@ -475,6 +559,9 @@ def main() -> int:
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT_MD"))
     ap.add_argument("--summarize-pmc", nargs=5,
                     metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV", "CALIB_WRITE_CSV", "OUT"))
+    ap.add_argument("--summarize-kernels", nargs=7,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV", "CALIB_WRITE_CSV", "MFMA_CSV",
+                             "STATS_CSV", "OUT"))
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     args = ap.parse_args()
     if args.summarize_stats:
@@ -482,6 +569,9 @@ def main() -> int:
         return 0
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.command)
+        return 0
+    if args.summarize_kernels:
+        summarize_kernels(*args.summarize_kernels, args.command, args.workload)
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
