@@ -276,17 +276,31 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X,
                              moe_stream copy);
 
 /*
- * Gate/up packing (section 3.3, "Offline NPU-Consumable Weight Layout":
- * experts are stored in the layout the kernels consume). One expert's gate
- * W_g [f][d] and up W_u [f][d] become one [2f][d] slice whose rows alternate
- * in blocks of 32: rows 64q..64q+31 are gate rows 32q..32q+31 and rows
- * 64q+32..64q+63 are up rows 32q..32q+31. The down slice is W_d [d][f]
- * unchanged.
- * moe_pack_gate_up: device, n experts, source expert stride src_stride and
- * destination stride dst_stride (elements; bytes for MOE_DT_BF16_FP8W, whose
- * W_g and W_u slices are [f][d] codes followed by [f] row scales each, and
- * whose packed slice gets its 2f row scales in the packed row order).
- * moe_pack_gate_up_host: the same on host memory, synchronous.
+ * Weight packing (section 3.3, "Offline NPU-Consumable Weight Layout":
+ * experts are stored in the layout the kernels consume).
+ *
+ * Tiled slice layout. A slice [N][K] (gate/up: N = 2f, K = d; down: N = d,
+ * K = f) is stored in blocks of 256 rows (the last block may be shorter);
+ * within a block, K is cut into pieces of 32 elements (the last piece is
+ * narrower when K % 32 != 0), stored piece after piece, each piece holding
+ * the block's rows one after another. Element (n, k) is at element offset
+ *   256*b*K + (k/32)*rows_b*32 + (n%256)*w + k%32,
+ * b = n/256, rows_b = min(256, N - 256*b), w = min(32, K - 32*(k/32)).
+ * The slice has exactly N*K elements. One K step of a 256-row weight tile is
+ * thus one contiguous run (16 KB for bf16), which streams from HBM about 1.5
+ * times faster than the same bytes read as 64-byte pieces of 256 rows.
+ *
+ * Gate/up: expert gate W_g [f][d] and up W_u [f][d] become one [2f][d]
+ * slice whose rows alternate in blocks of 32: rows 64q..64q+31 are gate rows
+ * 32q..32q+31 and rows 64q+32..64q+63 are up rows 32q..32q+31; that slice is
+ * stored tiled. Down: W_d [d][f] stored tiled.
+ * moe_pack_gate_up / moe_pack_down: device, n experts, source expert stride
+ * src_stride and destination stride dst_stride (elements; bytes for
+ * MOE_DT_BF16_FP8W, whose source slices are row-major codes followed by one
+ * fp32 scale per row, and whose packed slices keep their row scales after
+ * the codes, in the packed row order and untiled).
+ * moe_pack_gate_up_host / moe_pack_down_host: the same on host memory, one
+ * expert, synchronous.
  */
 moe_status moe_pack_gate_up(const moe_shape *shape, const void *W_g,
                             const void *W_u, void *dst, int32_t n,
@@ -294,11 +308,18 @@ moe_status moe_pack_gate_up(const moe_shape *shape, const void *W_g,
                             moe_stream stream);
 moe_status moe_pack_gate_up_host(const moe_shape *shape, const void *W_g,
                                  const void *W_u, void *dst);
+moe_status moe_pack_down(const moe_shape *shape, const void *W_d, void *dst,
+                         int32_t n, int64_t src_stride, int64_t dst_stride,
+                         moe_stream stream);
+moe_status moe_pack_down_host(const moe_shape *shape, const void *W_d,
+                              void *dst);
 
 /*
  * Slot arena (Eq. 3: the slice j of slot s starts at plane_j + s * S_j).
- *   plane_gu  device, P slots of [2f][d] dtype, slot stride stride_gu
- *   plane_d   device, P slots of [d][f] dtype, slot stride stride_d
+ *   plane_gu  device, P slots of packed gate/up slices (2f*d elements,
+ *             tiled layout above), slot stride stride_gu
+ *   plane_d   device, P slots of packed down slices (d*f elements, tiled),
+ *             slot stride stride_d
  *   (MOE_DT_BF16_FP8W: each slice is its codes then its row scales, and the
  *   strides are in bytes: stride_gu >= 2f*d + 8f, stride_d >= d*f + 4d)
  *   G         slots per bank (1 <= G <= P, P % G == 0); banks are used when
@@ -312,8 +333,8 @@ void moe_arena_destroy(moe_arena *arena);
 
 /*
  * Load expert `expert` into `slot`: Available/Ready/In-use -> Filling ->
- * Ready. src_gu ([2f][d], packed) and src_d ([d][f]) are host (pinned) or
- * device pointers; the copies run on copy_stream after the slot's previous
+ * Ready. src_gu and src_d (packed slices, as moe_pack_gate_up and
+ * moe_pack_down write them) are host (pinned) or device pointers; the copies run on copy_stream after the slot's previous
  * release (if any), and the slot's ready event is recorded after them. The
  * slot's previous mapping is withdrawn first. MOE_ERR_SLOT_STATE if the
  * expert is mapped to another slot or the slot is Filling.

@@ -72,6 +72,8 @@ _SIGS = {
     "moe_layer_prefill": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP], _I32),
     "moe_pack_gate_up": ([_VP, _VP, _VP, _VP, _I32, _I64, _I64, _VP], _I32),
     "moe_pack_gate_up_host": ([_VP, _VP, _VP, _VP], _I32),
+    "moe_pack_down": ([_VP, _VP, _VP, _I32, _I64, _I64, _VP], _I32),
+    "moe_pack_down_host": ([_VP, _VP, _VP], _I32),
     "moe_arena_create": ([_VP, _VP, _VP, _VP, _I64, _I64, _I32], _I32),
     "moe_arena_destroy": ([_VP], None),
     "arena_bind_slot": ([_VP, _I32, _I32, _VP, _VP, _VP], _I32),
@@ -228,6 +230,15 @@ def moe_pack_gate_up_host(shape, Wg, Wu, dst):
     _check(load().moe_pack_gate_up_host(ctypes.byref(shape), _ptr(Wg), _ptr(Wu), _ptr(dst)))
 
 
+def moe_pack_down(shape, Wd, dst, n, src_stride, dst_stride, stream=None):
+    _check(load().moe_pack_down(ctypes.byref(shape), _ptr(Wd), _ptr(dst), n, src_stride, dst_stride,
+                                _stream(stream)))
+
+
+def moe_pack_down_host(shape, Wd, dst):
+    _check(load().moe_pack_down_host(ctypes.byref(shape), _ptr(Wd), _ptr(dst)))
+
+
 def moe_arena_create(shape, plane_gu, plane_d, stride_gu, stride_d, G) -> int:
     h = ctypes.c_void_p(0)
     _check(load().moe_arena_create(ctypes.byref(h), ctypes.byref(shape), _ptr(plane_gu), _ptr(plane_d),
@@ -332,7 +343,7 @@ class Arena:
                 continue
             g, u, dn = expert_slices(Wg, Wu, Wd, scales, e)
             moe_pack_gate_up(self.shape, g, u, self.plane_gu[s], 1, 0, 0, stream)
-            self.plane_d[s].copy_(dn.reshape(self.plane_d[s].shape))
+            moe_pack_down(self.shape, dn, self.plane_d[s], 1, 0, 0, stream)
             arena_publish_slot(self, s, e, stream)
 
 

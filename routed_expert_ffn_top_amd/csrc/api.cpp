@@ -556,16 +556,46 @@ moe_status moe_pack_gate_up_host(const moe_shape *shape, const void *W_g, const 
     if (!W_g || !W_u || !dst) return fail(MOE_ERR_INVALID_ARG, "pack: NULL pointer");
     const size_t esz = (size_t)w_esz(*shape);
     const size_t row = (size_t)shape->d * esz;
-    const int f = shape->f;
+    const int f = shape->f, d = shape->d;
     for (int r = 0; r < 2 * f; ++r) {
         const int q = r / 64, w = r % 64;
         const int sr = w < 32 ? 32 * q + w : 32 * q + w - 32;   // source row of gate (w < 32) or up
         const char *src = (const char *)(w < 32 ? W_g : W_u) + (size_t)sr * row;
-        memcpy((char *)dst + (size_t)r * row, src, row);
-        if (w_fp8(*shape))   // row scales follow the codes, in the same row order
+        for (int k = 0; k < d; ++k)   // element (r, k) of the tiled [2f][d] slice
+            memcpy((char *)dst + (size_t)wtile_off(r, k, 2 * f, d) * esz, src + (size_t)k * esz, esz);
+        if (w_fp8(*shape))   // row scales follow the codes, in the packed row order
             memcpy((char *)dst + (size_t)2 * f * row + (size_t)r * 4,
                    (const char *)(w < 32 ? W_g : W_u) + (size_t)f * row + (size_t)sr * 4, 4);
     }
+    return MOE_OK;
+}
+
+moe_status moe_pack_down(const moe_shape *shape, const void *W_d, void *dst, int32_t n, int64_t src_stride,
+                         int64_t dst_stride, moe_stream stream)
+{
+    MOE_TRY(check_shape(shape));
+    if (!W_d || !dst || n < 0) return fail(MOE_ERR_INVALID_ARG, "pack: bad arguments");
+    const int esz = w_esz(*shape);
+    if (n > 1 && ((size_t)src_stride * esz < d_slice_bytes(*shape) || (size_t)dst_stride * esz < d_slice_bytes(*shape)))
+        return fail(MOE_ERR_INVALID_ARG, "pack: strides smaller than a slice");
+    if (((src_stride * esz) % 4) != 0 || ((dst_stride * esz) % 4) != 0)
+        return fail(MOE_ERR_INVALID_ARG, "pack: strides must be whole 32-bit words");
+    HIP_TRY(launch_pack_down(*shape, W_d, dst, n, src_stride, dst_stride, S(stream)), "pack launch");
+    return MOE_OK;
+}
+
+moe_status moe_pack_down_host(const moe_shape *shape, const void *W_d, void *dst)
+{
+    MOE_TRY(check_shape(shape));
+    if (!W_d || !dst) return fail(MOE_ERR_INVALID_ARG, "pack: NULL pointer");
+    const size_t esz = (size_t)w_esz(*shape);
+    const int d = shape->d, f = shape->f;
+    for (int m = 0; m < d; ++m)
+        for (int k = 0; k < f; ++k)   // element (m, k) of the tiled [d][f] slice
+            memcpy((char *)dst + (size_t)wtile_off(m, k, d, f) * esz,
+                   (const char *)W_d + ((size_t)m * f + k) * esz, esz);
+    if (w_fp8(*shape))   // the [d] row scales follow the codes unchanged
+        memcpy((char *)dst + (size_t)d * f, (const char *)W_d + (size_t)d * f, (size_t)d * 4);
     return MOE_OK;
 }
 

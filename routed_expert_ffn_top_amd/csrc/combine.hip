@@ -61,16 +61,19 @@ __global__ __launch_bounds__(256) void k_combine(float *__restrict__ Y, int64_t 
     *(float4 *)(Y + (int64_t)t * ldy + c) = y;
 }
 
-// dst row r of expert e: q = r / 64, w = r % 64; gate row 32q + w for w < 32,
-// up row 32q + w - 32 otherwise. One workgroup copies one row as 32-bit words.
-// With row scales (fp8 weights: src_scale_w > 0), the row's fp32 scale moves
-// with it: from word src_scale_w + source row of the source slice to word
-// dst_scale_w + r of the packed slice.
+// Packed gate/up row r of expert e: q = r / 64, w = r % 64; gate row 32q + w
+// for w < 32, up row 32q + w - 32 otherwise, written in the tiled layout
+// (wtile_off over the [2f][d] slice). One workgroup copies one row as 32-bit
+// words (epw elements each; a word never straddles a K piece). With row
+// scales (fp8 weights: src_scale_w > 0), the row's fp32 scale moves with it:
+// from word src_scale_w + source row of the source slice to word
+// dst_scale_w + r of the packed slice (scales stay in row order).
 __global__ __launch_bounds__(256) void k_pack_gate_up(const uint32_t *__restrict__ Wg,
                                                       const uint32_t *__restrict__ Wu,
                                                       uint32_t *__restrict__ dst, int64_t row_words,
                                                       int64_t src_stride_w, int64_t dst_stride_w,
-                                                      int64_t src_scale_w, int64_t dst_scale_w)
+                                                      int64_t src_scale_w, int64_t dst_scale_w, int N, int K,
+                                                      int epw)
 {
     const int r = blockIdx.x;
     const int e = blockIdx.y;
@@ -78,10 +81,25 @@ __global__ __launch_bounds__(256) void k_pack_gate_up(const uint32_t *__restrict
     const int sr = w < 32 ? 32 * q + w : 32 * q + w - 32;
     const uint32_t *slice = (w < 32 ? Wg : Wu) + (int64_t)e * src_stride_w;
     const uint32_t *src = slice + (int64_t)sr * row_words;
-    uint32_t *out = dst + (int64_t)e * dst_stride_w + (int64_t)r * row_words;
-    for (int64_t c = threadIdx.x; c < row_words; c += 256) out[c] = src[c];
+    uint32_t *out = dst + (int64_t)e * dst_stride_w;
+    for (int64_t c = threadIdx.x; c < row_words; c += 256) out[wtile_off(r, c * epw, N, K) / epw] = src[c];
     if (src_scale_w > 0 && threadIdx.x == 0)
         dst[(int64_t)e * dst_stride_w + dst_scale_w + r] = slice[src_scale_w + sr];
+}
+
+// Down row m of expert e ([d][f] slice, row m = output column m) into the
+// tiled layout; fp8 row scales (src_scale_w > 0) are copied in row order.
+__global__ __launch_bounds__(256) void k_pack_down(const uint32_t *__restrict__ Wd, uint32_t *__restrict__ dst,
+                                                   int64_t row_words, int64_t src_stride_w, int64_t dst_stride_w,
+                                                   int64_t scale_w, int N, int K, int epw)
+{
+    const int m = blockIdx.x;
+    const int e = blockIdx.y;
+    const uint32_t *slice = Wd + (int64_t)e * src_stride_w;
+    const uint32_t *src = slice + (int64_t)m * row_words;
+    uint32_t *out = dst + (int64_t)e * dst_stride_w;
+    for (int64_t c = threadIdx.x; c < row_words; c += 256) out[wtile_off(m, c * epw, N, K) / epw] = src[c];
+    if (scale_w > 0 && threadIdx.x == 0) out[scale_w + m] = slice[scale_w + m];
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -149,7 +167,20 @@ hipError_t launch_pack_gate_up(const moe_shape &s, const void *Wg, const void *W
     const int64_t dscale = w_fp8(s) ? (int64_t)2 * s.f * row_words : 0;
     hipLaunchKernelGGL(k_pack_gate_up, dim3((unsigned)(2 * s.f), (unsigned)n), dim3(256), 0, st,
                        (const uint32_t *)Wg, (const uint32_t *)Wu, (uint32_t *)dst, row_words, ssw,
-                       dsw, sscale, dscale);
+                       dsw, sscale, dscale, 2 * s.f, s.d, 4 / esz);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_down(const moe_shape &s, const void *Wd, void *dst, int n, int64_t src_stride,
+                            int64_t dst_stride, hipStream_t st)
+{
+    if (n == 0) return hipSuccess;
+    const int esz = w_esz(s);
+    const int64_t row_words = (int64_t)s.f * esz / 4;
+    const int64_t ssw = src_stride * esz / 4, dsw = dst_stride * esz / 4;
+    const int64_t scale = w_fp8(s) ? (int64_t)s.d * row_words : 0;   // [d] scales after the [d][f] codes
+    hipLaunchKernelGGL(k_pack_down, dim3((unsigned)s.d, (unsigned)n), dim3(256), 0, st, (const uint32_t *)Wd,
+                       (uint32_t *)dst, row_words, ssw, dsw, scale, s.d, s.f, 4 / esz);
     return hipGetLastError();
 }
 

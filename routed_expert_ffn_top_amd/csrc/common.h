@@ -49,6 +49,25 @@ inline size_t d_slice_bytes(const moe_shape &s)
     return (size_t)s.d * s.f * w_esz(s) + (w_fp8(s) ? (size_t)s.d * 4 : 0);
 }
 
+// Tiled layout of an expert weight slice [N][K] in the arena (section 3.3:
+// weights are stored offline in the order the kernels consume them). Rows
+// form blocks of kWRows; within a block, K is cut into pieces of kWK
+// elements (the last piece narrower when K % kWK != 0) stored piece-major,
+// each piece holding the block's rows one after another, so that one K step
+// of a 256-row weight tile is one contiguous run (16 KB for bf16). Element
+// (n, k) sits at element offset
+//   kWRows*nb*K + (k / kWK)*rows_nb*kWK + (n % kWRows)*w + k % kWK,
+// nb = n / kWRows, rows_nb = min(kWRows, N - kWRows*nb), w = min(kWK, K -
+// kWK*(k / kWK)) the width of k's piece. The slice keeps its size.
+constexpr int kWRows = 256, kWK = 32;
+__host__ __device__ inline int64_t wtile_off(int64_t n, int64_t k, int64_t N, int64_t K)
+{
+    const int64_t nb = n / kWRows, kp = k / kWK;
+    const int64_t rows = N - nb * kWRows < kWRows ? N - nb * kWRows : kWRows;
+    const int64_t w = K - kp * kWK < kWK ? K - kp * kWK : kWK;
+    return nb * kWRows * K + kp * rows * kWK + (n % kWRows) * w + k % kWK;
+}
+
 // Splits of the down projection's K = f: when the down tiles (about
 // experts x row blocks x d/256) would not fill the GPU, each tile's K range
 // is cut in S pieces whose partial products go to S separate per-route rows,
@@ -128,6 +147,8 @@ hipError_t launch_combine(const moe_shape &s, float *Y, const float *Yr, const i
                           hipStream_t st);   // sums the down_splits(s) partial rows of each route
 hipError_t launch_pack_gate_up(const moe_shape &s, const void *Wg, const void *Wu, void *dst,
                                int n, int64_t src_stride, int64_t dst_stride, hipStream_t st);
+hipError_t launch_pack_down(const moe_shape &s, const void *Wd, void *dst, int n, int64_t src_stride,
+                            int64_t dst_stride, hipStream_t st);
 hipError_t launch_selftest_mfma(float *out, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, int64_t n, hipStream_t st);
 hipError_t launch_expert_hist(const moe_shape &s, const int32_t *idx, int64_t n, int32_t *count,

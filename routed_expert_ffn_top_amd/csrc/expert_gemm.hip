@@ -229,6 +229,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     static_assert(BM % (16 * NW) == 0 && (BN * BROW) % (1024 * NW) == 0 && MI >= 1 && NI >= 1, "tile");
     static_assert(!GATEUP || (TN % 64) == 0, "gate/up pairs need 64-column wave tiles");
     static_assert(NS >= 3, "the ring needs at least 3 stages");
+    static_assert(BK == kWK && kWRows % BN == 0, "a B stage is one K piece of one row block of the tiled layout");
 
     __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
     __shared__ int32_t s_route[2][GATEUP ? 1 : BM];   // by tile parity
@@ -300,6 +301,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     // .. +15 of A (and likewise of B); lane -> row + l/4, chunk position l%4
     const char *asrc[AI];
     const char *bsrc[BI];
+    int bstep = 0;   // bytes from one stage of B to the next (tiled layout)
     const int lr = lane >> 2, lp = lane & 3;
     // A row of each of this lane's copies (gathered token rows for gate/up)
     auto fetch_rows = [&](const TileInfo &t, int32_t *rows) {
@@ -316,7 +318,15 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
             const int c = lp ^ ((r >> 2) & 3);
             asrc[j] = (const char *)a.A + ((int64_t)rows[j] * a.lda + (int64_t)t.ks * Kc) * 2 + c * 16;
         }
+        // The slice is in the tiled layout (wtile_off): the tile's columns lie in
+        // one 256-row block whose K pieces of 32 are stored piece after piece,
+        // so each stage of B is one contiguous run of rows_nb * 32 elements
+        // and the next stage starts bstep bytes further on.
         const char *Bslot = (const char *)a.B + (int64_t)t.slot * a.slot_stride * BESZ;
+        const int nb = t.n0 / kWRows;
+        const int rows_nb = min(kWRows, N - nb * kWRows);
+        bstep = rows_nb * BK * BESZ;
+        const char *Bblk = Bslot + ((int64_t)nb * kWRows * K + (int64_t)(t.ks * Kc / BK) * rows_nb * BK) * BESZ;
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
             if constexpr (BF8) {
@@ -325,12 +335,12 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                 const int r = (wave * BI + j) * 32 + (lane >> 1);
                 const int c = (lane & 1) ^ ((r >> 3) & 1);
                 const int n = min(t.n0 + r, N - 1);
-                bsrc[j] = Bslot + (int64_t)n * K + (int64_t)t.ks * Kc + c * 16;
+                bsrc[j] = Bblk + (int64_t)(n - nb * kWRows) * BK + c * 16;
             } else {
                 const int r = (wave * BI + j) * 16 + lr;
                 const int c = lp ^ ((r >> 2) & 3);
                 const int n = min(t.n0 + r, N - 1);
-                bsrc[j] = Bslot + ((int64_t)n * K + (int64_t)t.ks * Kc) * 2 + c * 16;
+                bsrc[j] = Bblk + (int64_t)(n - nb * kWRows) * BK * 2 + c * 16;
             }
         }
     };
@@ -369,7 +379,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                                              (LDS_AS void *)(st + (wave * AI + j) * 1024), 16, 0, 0);
 #pragma unroll
         for (int j = 0; j < BI; ++j)
-            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(bsrc[j] + kt * BK * BESZ),
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(bsrc[j] + (int64_t)kt * bstep),
                                              (LDS_AS void *)(st + BM * ROWB + (wave * BI + j) * 1024), 16, 0,
                                              0);
     };
@@ -622,7 +632,9 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a)
     const int rr = min(lr, rows - 1);
     const TE *ap = (GATEUP ? (const TE *)a.A + (int64_t)a.rec_token[row0 + rr] * a.lda
                            : (const TE *)a.A + (int64_t)(row0 + rr) * a.lda) + kb;
-    const TE *bp = (const TE *)a.B + (int64_t)slot * a.slot_stride + (int64_t)min(n0 + lr, N - 1) * a.K + kb;
+    // B row n of the slice, in the tiled layout (wtile_off)
+    const TE *bslice = (const TE *)a.B + (int64_t)slot * a.slot_stride;
+    const int64_t bn = min(n0 + lr, N - 1);
     if (!GATEUP && tid < BM) {
         const int rt = a.rec_route[row0 + min(tid, rows - 1)];
         s_route[tid] = rt;
@@ -640,7 +652,7 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a)
         for (int q = 0; q < 4; ++q) {
             const int kk = k0 + lk + q;
             As[lk + q][lr] = kk < K ? ld_f32<TE>(ap + kk) : 0.0f;
-            Bs[lk + q][lr] = kk < K ? ld_f32<TE>(bp + kk) : 0.0f;
+            Bs[lk + q][lr] = kk < K ? ld_f32<TE>(bslice + wtile_off(bn, kb + kk, N, a.K)) : 0.0f;
         }
         __syncthreads();
 #pragma unroll

@@ -60,11 +60,13 @@ class MoELayer:
             self.host_gu_plane = torch.empty((ne,) + gu_shape, dtype=self.arena.plane_gu.dtype, pin_memory=True)
             self.host_d_plane = torch.empty((ne,) + d_shape, dtype=self.arena.plane_d.dtype, pin_memory=True)
             tmp = torch.empty(gu_shape, dtype=self.arena.plane_gu.dtype, device=self.device)
+            tmp_d = torch.empty(d_shape, dtype=self.arena.plane_d.dtype, device=self.device)
             for e in range(ne):
                 g, u, dn = B.expert_slices(Wg, Wu, Wd, scales, e)
                 B.moe_pack_gate_up(self.shape, g, u, tmp, 1, 0, 0, stream)
+                B.moe_pack_down(self.shape, dn, tmp_d, 1, 0, 0, stream)
                 self.host_gu_plane[e].copy_(tmp)
-                self.host_d_plane[e].copy_(dn.reshape(d_shape))
+                self.host_d_plane[e].copy_(tmp_d)
             self.host_gu = [self.host_gu_plane[e] for e in range(ne)]
             self.host_d = [self.host_d_plane[e] for e in range(ne)]
             self.phi = None

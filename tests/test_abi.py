@@ -125,28 +125,80 @@ def test_route_build_argument_checks():
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
 
 
+def _untile(flat, N, K):
+    """[N][K] view of a slice stored in the tiled layout include/moe.h states:
+    256-row blocks; in a block, pieces of 32 along K (the last narrower),
+    piece after piece, each holding the block's rows one after another."""
+    flat = np.asarray(flat).reshape(-1)
+    assert flat.size == N * K
+    out = np.empty((N, K), dtype=flat.dtype)
+    for b0 in range(0, N, 256):
+        rows = min(256, N - b0)
+        base = b0 * K
+        for k0 in range(0, K, 32):
+            w = min(32, K - k0)
+            piece = flat[base + k0 * rows: base + k0 * rows + rows * w].reshape(rows, w)
+            out[b0:b0 + rows, k0:k0 + w] = piece
+    return out
+
+
+def test_untile_helper_on_a_hand_case():
+    """The decoder above on a 2-block, ragged case worked by hand: N = 258,
+    K = 36, element (n, k) at 256*b*K + (k//32)*rows*32 + (n%256)*w + k%32."""
+    N, K = 258, 36
+    flat = np.empty(N * K, dtype=np.int64)
+    for n in range(N):
+        for k in range(K):
+            b, kp = n // 256, k // 32
+            rows, w = min(256, N - 256 * b), min(32, K - 32 * kp)
+            flat[256 * b * K + kp * rows * 32 + (n % 256) * w + k % 32] = 1000 * n + k
+    assert np.array_equal(_untile(flat, N, K), 1000 * np.arange(N)[:, None] + np.arange(K)[None, :])
+    # spot values: row 257 (block 1, 2 rows), k = 33 (second piece, width 4)
+    assert flat[256 * K + 1 * 2 * 32 + 1 * 4 + 1] == 257 * 1000 + 33
+
+
 def test_pack_gate_up_host_layout():
-    """Rows 64q..64q+31 of the packed slice are gate rows 32q..32q+31, rows
-    64q+32..64q+63 are up rows 32q..32q+31 (the layout include/moe.h states)."""
-    f, d = 96 * 2, 64
+    """Packed rows 64q..64q+31 are gate rows 32q..32q+31, rows 64q+32..64q+63
+    are up rows 32q..32q+31, and the [2f][d] slice is stored tiled (the
+    layout include/moe.h states); d = 100 leaves a narrower last K piece."""
+    f, d = 96 * 2, 100
     s = B.make_shape(T=4, d=d, f=f, E=4, k=1, dtype="f32")
     rng = np.random.default_rng(0)
     Wg = torch.from_numpy(rng.standard_normal((f, d), dtype=np.float32))
     Wu = torch.from_numpy(rng.standard_normal((f, d), dtype=np.float32))
     out = torch.empty((2 * f, d), dtype=torch.float32)
     B.moe_pack_gate_up_host(s, Wg, Wu, out)
+    rows = torch.from_numpy(_untile(out.numpy(), 2 * f, d))
     for q in range(f // 32):
-        assert torch.equal(out[64 * q:64 * q + 32], Wg[32 * q:32 * q + 32])
-        assert torch.equal(out[64 * q + 32:64 * q + 64], Wu[32 * q:32 * q + 32])
-    sb = B.make_shape(T=4, d=d, f=f, E=4, k=1, dtype="bf16")
-    outb = torch.empty((2 * f, d), dtype=torch.bfloat16)
-    B.moe_pack_gate_up_host(sb, Wg.bfloat16(), Wu.bfloat16(), outb)
-    assert torch.equal(outb[32:64], Wu[:32].bfloat16())
+        assert torch.equal(rows[64 * q:64 * q + 32], Wg[32 * q:32 * q + 32])
+        assert torch.equal(rows[64 * q + 32:64 * q + 64], Wu[32 * q:32 * q + 32])
+    db = 128
+    sb = B.make_shape(T=4, d=db, f=f, E=4, k=1, dtype="bf16")
+    Wgb = torch.from_numpy(rng.standard_normal((f, db), dtype=np.float32)).bfloat16()
+    Wub = torch.from_numpy(rng.standard_normal((f, db), dtype=np.float32)).bfloat16()
+    outb = torch.empty((2 * f, db), dtype=torch.bfloat16)
+    B.moe_pack_gate_up_host(sb, Wgb, Wub, outb)
+    rowsb = _untile(outb.view(torch.int16).numpy(), 2 * f, db)
+    assert np.array_equal(rowsb[32:64], Wub[:32].view(torch.int16).numpy())
+    assert np.array_equal(rowsb[256:288], Wgb[128:160].view(torch.int16).numpy())
+
+
+def test_pack_down_host_layout():
+    """The down slice W_d [d][f] is stored tiled, nothing else changes;
+    d = 300 gives a short second 256-row block."""
+    d, f = 300, 96
+    s = B.make_shape(T=4, d=d, f=f, E=4, k=1, dtype="f32")
+    rng = np.random.default_rng(2)
+    Wd = rng.standard_normal((d, f), dtype=np.float32)
+    out = torch.empty((d, f), dtype=torch.float32)
+    B.moe_pack_down_host(s, torch.from_numpy(Wd), out)
+    assert np.array_equal(_untile(out.numpy(), d, f), Wd)
+    assert out.numpy().reshape(-1)[256 * f + 1 * 44 * 32 + 3 * 32 + 5] == Wd[256 + 3, 32 + 5]
 
 
 def test_pack_gate_up_host_fp8_rows_and_scales():
-    """fp8 weights: the packed slice is the permuted code rows followed by
-    the rows' fp32 scales in the same permuted order."""
+    """fp8 weights: the packed slice is the permuted code rows, tiled,
+    followed by the rows' fp32 scales in the same permuted order."""
     f, d = 128, 64
     s = B.make_shape(T=4, d=d, f=f, E=4, k=1, dtype="bf16_fp8w")
     assert B.moe_workspace_bytes(s) > 0
@@ -160,13 +212,27 @@ def test_pack_gate_up_host_fp8_rows_and_scales():
     out = torch.empty(2 * f * d + 8 * f, dtype=torch.uint8)
     B.moe_pack_gate_up_host(s, src_g, src_u, out)
     o = out.numpy()
-    rows = o[:2 * f * d].reshape(2 * f, d)
+    rows = _untile(o[:2 * f * d], 2 * f, d)
     scales = o[2 * f * d:].view(np.float32)
     for q in range(f // 32):
         assert np.array_equal(rows[64 * q:64 * q + 32], codes_g[32 * q:32 * q + 32])
         assert np.array_equal(rows[64 * q + 32:64 * q + 64], codes_u[32 * q:32 * q + 32])
         assert np.array_equal(scales[64 * q:64 * q + 32], sc_g[32 * q:32 * q + 32])
         assert np.array_equal(scales[64 * q + 32:64 * q + 64], sc_u[32 * q:32 * q + 32])
+
+
+def test_pack_down_host_fp8_codes_and_scales():
+    d, f = 320, 64
+    s = B.make_shape(T=4, d=d, f=f, E=4, k=1, dtype="bf16_fp8w")
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 256, size=(d, f), dtype=np.uint8)
+    sc = rng.random(d, dtype=np.float32)
+    src = torch.from_numpy(np.concatenate([codes.reshape(-1), sc.view(np.uint8)]))
+    out = torch.empty(d * f + 4 * d, dtype=torch.uint8)
+    B.moe_pack_down_host(s, src, out)
+    o = out.numpy()
+    assert np.array_equal(_untile(o[:d * f], d, f), codes)
+    assert np.array_equal(o[d * f:].view(np.float32), sc)
 
 
 def test_arena_fp8_strides_are_bytes_and_cover_the_scales():

@@ -115,18 +115,23 @@ def test_fp8w_edge_shapes():
 
 @pytest.mark.parametrize("dtype", ["bf16", "bf16_fp8w"])
 def test_device_pack_equals_host_pack(dtype):
-    say(f"gate/up packing on the device equals the host packing ({dtype})")
+    say(f"gate/up and down packing on the device equal the host packing ({dtype})")
     cfg = MID.with_(dtype=dtype, E=3, k=2, T=4)
     inp = gpu_inputs(cfg)
     s = B.make_shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, P=cfg.E, dtype=dtype)
     arena = B.Arena(s)
     scales = (inp.Sg, inp.Su, inp.Sd) if cfg.fp8_weights else None
     for e in range(cfg.E):
-        g, u, _ = B.expert_slices(inp.Wg, inp.Wu, inp.Wd, scales, e)
+        g, u, dn = B.expert_slices(inp.Wg, inp.Wu, inp.Wd, scales, e)
         dev = torch.empty_like(arena.plane_gu[0])
         B.moe_pack_gate_up(s, g, u, dev, 1, 0, 0)
         host = torch.empty_like(dev, device="cpu")
         B.moe_pack_gate_up_host(s, g.cpu(), u.cpu(), host)
+        dev_d = torch.empty_like(arena.plane_d[0])
+        B.moe_pack_down(s, dn, dev_d, 1, 0, 0)
+        host_d = torch.empty_like(dev_d, device="cpu")
+        B.moe_pack_down_host(s, dn.cpu(), host_d)
         torch.cuda.synchronize()
-        assert torch.equal(dev.cpu().view(torch.uint8), host.view(torch.uint8)), f"expert {e}"
+        assert torch.equal(dev.cpu().view(torch.uint8), host.view(torch.uint8)), f"gate/up expert {e}"
+        assert torch.equal(dev_d.cpu().view(torch.uint8), host_d.view(torch.uint8)), f"down expert {e}"
     arena.close()
