@@ -301,7 +301,8 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     // .. +15 of A (and likewise of B); lane -> row + l/4, chunk position l%4
     const char *asrc[AI];
     const char *bsrc[BI];
-    int bstep = 0;   // bytes from one stage of B to the next (tiled layout)
+    int bstep = 0;       // bytes from one stage of B to the next (tiled layout)
+    int astep = BK * 2;  // likewise for A (gathered X rows: 64 bytes; H: the block's piece)
     const int lr = lane >> 2, lp = lane & 3;
     // A row of each of this lane's copies (gathered token rows for gate/up)
     auto fetch_rows = [&](const TileInfo &t, int32_t *rows) {
@@ -316,8 +317,18 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         for (int j = 0; j < AI; ++j) {
             const int r = (wave * AI + j) * 16 + lr;
             const int c = lp ^ ((r >> 2) & 3);
-            asrc[j] = (const char *)a.A + ((int64_t)rows[j] * a.lda + (int64_t)t.ks * Kc) * 2 + c * 16;
+            if (GATEUP) {
+                asrc[j] = (const char *)a.A + ((int64_t)rows[j] * a.lda + (int64_t)t.ks * Kc) * 2 + c * 16;
+            } else {
+                // H rows of this tile's row block, stored block-tiled (see the
+                // gate/up epilogue): K pieces of 32 one after another
+                const int rr = rows[j] - t.row0;
+                asrc[j] = (const char *)a.A +
+                          ((int64_t)t.row0 * a.lda + (int64_t)(t.ks * Kc / BK) * t.rows * BK + (int64_t)rr * BK) * 2 +
+                          c * 16;
+            }
         }
+        astep = GATEUP ? BK * 2 : t.rows * BK * 2;
         // The slice is in the tiled layout (wtile_off): the tile's columns lie in
         // one 256-row block whose K pieces of 32 are stored piece after piece,
         // so each stage of B is one contiguous run of rows_nb * 32 elements
@@ -372,7 +383,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     };
     auto issue = [&](int kt) {
         char *st = lds + (kt % NS) * STAGE;
-        const int kb = kt * BK * 2;
+        const int64_t kb = (int64_t)kt * astep;
 #pragma unroll
         for (int j = 0; j < AI; ++j)
             __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(asrc[j] + kb),
@@ -546,12 +557,18 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                 uint16_t *H = (uint16_t *)a.C;
                 const int fN = N / 2;
                 const int fc0 = ((cur.n0 + wn * TN) / 64) * 32 + cpair;   // first H column pair
+                // H is stored block-tiled: the records of this tile's row block
+                // (row0 .. row0+rows-1) occupy the same span as row-major, with
+                // their columns cut into pieces of 32 stored piece after piece,
+                // so that each K step of the down tile reads one contiguous run.
+                uint16_t *hbase = H + (int64_t)cur.row0 * a.ldc + (int64_t)(fc0 / BK) * cur.rows * BK + (fc0 % BK);
+                const int qstep = cur.rows * BK;
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
 #pragma unroll
                     for (int r = 0; r < 16; r += 2) {
                         const int m = wm * TM + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3) + (even ? 0 : 1);
-                        uint16_t *hrow = H + (int64_t)(cur.row0 + (checked ? min(m, cur.rows - 1) : m)) * a.ldc + fc0;
+                        const int mm = checked ? min(m, cur.rows - 1) : m;
 #pragma unroll
                         for (int q = 0; q < NI / 2; ++q) {
                             const float s0 = BF8 ? silu_mul_fast(acc[i][2 * q][r] * sc[2 * q], acc[i][2 * q + 1][r] * sc[2 * q + 1])
@@ -561,7 +578,8 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
                             const float y = __int_as_float(
                                 __builtin_amdgcn_mov_dpp(__float_as_int(even ? s1 : s0), 0xB1, 0xF, 0xF, false));
                             const uint32_t packed = even ? pack_bf16x2(s0, y) : pack_bf16x2(y, s1);
-                            if (!checked || (m < cur.rows && fc0 + q * 32 < fN)) *(uint32_t *)(hrow + q * 32) = packed;
+                            if (!checked || (m < cur.rows && fc0 + q * 32 < fN))
+                                *(uint32_t *)(hbase + q * qstep + mm * BK) = packed;
                         }
                     }
                 }
@@ -605,7 +623,9 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
 
 // ---------------------------------------------------------------------------
 // Plain LDS-tiled kernel (fp32 FMA on the vector ALUs) for fp32 layers; also
-// runs bf16 inputs as an independent second path. 64x64 tiles, K step 16,
+// runs bf16 inputs as an independent second path (its H is row-major [C][f];
+// the ring kernels' H is block-tiled, and a call always runs both
+// projections with the same kernel). 64x64 tiles, K step 16,
 // 256 threads with 4x4 outputs each. For gate/up a thread owns columns
 // {2tx, 2tx+1} (gate) and {32+2tx, 32+2tx+1} (up) of its 64-column block, so
 // both halves of each SwiGLU pair are in one thread.
