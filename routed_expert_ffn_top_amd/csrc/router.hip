@@ -102,14 +102,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int h = 0; h < 2; ++h) rslot[v][h] = (4 * v + q) * 32 + ((2 * b + h + rot(q)) & 31);
     // this lane's two pieces of every group: slot S = (2 wave + k) * 64 + lane
-    const float *wsrc[2];
-    int wslot[2];
+    // holds 4 weights of expert row r at hidden index g * 128 + wcol[k]
+    const float *wrow_s[2];
+    int wslot[2], wcol[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int S = (2 * wave + k) * 64 + lane, r = S >> 5;
         const int p = ((S & 31) - rot(r)) & 31;   // 2 * run + half
         wslot[k] = S;
-        wsrc[k] = Wr + (int64_t)min(e0 + r, E - 1) * d + (p >> 1) * 8 + (p & 1) * 4;
+        wrow_s[k] = Wr + (int64_t)min(e0 + r, E - 1) * d;
+        wcol[k] = (p >> 1) * 8 + (p & 1) * 4;
     }
 
     const TX *xrow[TQ];
@@ -134,13 +136,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     };
     auto load_w = [&](int g, int k, u32x4_t (&wt)[2]) {
-        const int i = min(g, ng - 1) * 128;
-        if (FULL) {
-            wt[k] = *(const u32x4_t *)(wsrc[k] + i);
-        } else {
-            const int off = (int)(wsrc[k] - Wr) % d;   // hidden index of the piece in its row
-            wt[k] = *(const u32x4_t *)(wsrc[k] + (i + off < d ? i : -off));
-        }
+        const int i = min(g, ng - 1) * 128 + wcol[k];   // d % 4 == 0: a piece is inside the row or past it
+        wt[k] = *(const u32x4_t *)(wrow_s[k] + (FULL || i < d ? i : 0));
     };
     auto read_w = [&](int g, u32x4_t (&wv)[4][2]) {
         const u32x4_t *buf = wbuf[g % NB];
