@@ -215,6 +215,15 @@ def test_layer_tiny_fp32():
     _check_layer(CONFIGS["tiny_fp32"])
 
 
+def test_layer_ragged_weight_blocks():
+    """The tiled weight layout's short pieces: bf16 with d = 320 (the down
+    slice's second 256-row block has 64 rows) and fp32 with d = 100 (the
+    gate/up slice's last K piece is 4 wide, read by the plain kernel)."""
+    say("layer, ragged weight blocks")
+    _check_layer(MoEConfig(name="ragged_bf16", index=31, T=150, d=320, f=128, E=8, k=2))
+    _check_layer(MoEConfig(name="ragged_fp32", index=32, T=50, d=100, f=96, E=6, k=2, dtype="f32"))
+
+
 def test_layer_mid_bf16():
     say("layer mid bf16")
     _check_layer(MID)
