@@ -59,10 +59,13 @@ typedef void *moe_stream; /* a hipStream_t */
  * float: sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
  * S.1111.111 is NaN) with one fp32 scale per weight row, a weight being code
  * times its row's scale: the weight-only quantised experts of the pages'
- * quantised-weight path. Each slice ([2f][d] packed gate/up, or [d][f] down)
- * stores its codes row-major followed by its rows' fp32 scales ([2f] or
- * [d]); slot strides are then in bytes. The expert kernels decode the codes
- * to bf16 operands exactly and scale the fp32 accumulators. */
+ * quantised-weight path. A weight slice handed to the packing calls holds
+ * its codes row-major followed by its rows' fp32 scales; a packed slice in
+ * the arena ([2f][d] gate/up or [d][f] down) holds its codes in the tiled
+ * layout of the packing calls followed by its rows' scales ([2f] or [d]) in
+ * packed row order; slot strides are then in bytes. The expert kernels
+ * decode the codes to bf16 operands exactly and scale the fp32
+ * accumulators. */
 #define MOE_DT_BF16_FP8W 2
 
 /* Device error word bits (moe_device_errors). */
@@ -259,7 +262,8 @@ moe_status moe_expert_ffn(const moe_shape *shape, const void *X, float *Y,
  *   X, W_r, bias, logits, Y, routes, ws: as above (W_r/bias or logits).
  *   host_gu, host_d: NULL for a resident layer -- every expert must then be
  *     Ready in the arena. Otherwise arrays of E + n_shared host pointers to
- *     each expert's prepacked gate/up and down slices in pinned memory: the
+ *     each expert's packed gate/up and down slices (as moe_pack_gate_up and
+ *     moe_pack_down write them) in pinned memory: the
  *     experts are paged through the arena's banks of G slots on the copy
  *     stream, group by group, overlapped with compute (section 3.4), and
  *     groups with no routes are skipped. Paging synchronizes the compute
