@@ -33,6 +33,10 @@
  *                         point: sign, 4 exponent bits with bias 7, 3 mantissa
  *                         bits; exponent 0 is subnormal; S.1111.111 is NaN;
  *                         there are no infinities).
+ *   oracle_mxfp4_decode   the weights of an OCP MXFP4 slice: 4-bit E2M1 codes
+ *                         times one E8M0 power-of-two scale per 32 weights of
+ *                         a row (the 4-bit block-scaled weight format standing
+ *                         for the pages' 4-bit weight-only blocks).
  *
  * Parity status: every function is pinned by CPU tests (brute force, closed
  * forms, special cases and invariants); none is "parity unpinned".
@@ -205,6 +209,29 @@ int64_t oracle_route_map(int64_t kp, int64_t t0, int64_t nt, const int32_t *idx,
 }
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * MXFP4 (OCP Microscaling Formats, FP4 E2M1 elements with an E8M0 scale per
+ * block of 32). codes: [N][K/2] bytes; element 2i of a row is the low nibble
+ * of byte i, element 2i+1 the high nibble. An E2M1 code is sign (bit 3),
+ * exponent (bits 2..1, bias 1) and mantissa (bit 0): exponent 0 gives the
+ * subnormals 0 and 0.5, exponent e > 0 gives (1 + m/2) * 2^(e-1); there are
+ * no infinities or NaN. scales: [N][K/32] bytes, E8M0: 2^(s - 127), s = 255
+ * is NaN. out[n][k] = E2M1(code[n][k]) * 2^(scales[n][k/32] - 127).
+ */
+void oracle_mxfp4_decode(int64_t N, int64_t K, const uint8_t *codes, const uint8_t *scales, float *out)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const uint8_t byte = codes[n * (K / 2) + k / 2];
+            const int c = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+            const int sgn = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+            const double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+            const int sc = scales[n * (K / 32) + k / 32];
+            const double v = sc == 255 ? NAN : ldexp(sgn ? -mag : mag, sc - 127);
+            out[n * K + k] = (float)v;
+        }
+}
 
 /*
  * fp8 e4m3 codes to fp32 values (exact: every code's value has at most 4

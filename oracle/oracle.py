@@ -67,6 +67,8 @@ class Oracle:
         lib.oracle_expert_ffn.restype = None
         lib.oracle_fp8e4m3_decode.argtypes = [_i64, _ptr, _ptr]
         lib.oracle_fp8e4m3_decode.restype = None
+        lib.oracle_mxfp4_decode.argtypes = [_i64, _i64, _ptr, _ptr, _ptr]
+        lib.oracle_mxfp4_decode.restype = None
         lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -121,6 +123,18 @@ class Oracle:
         return dict(count=count, offset=offset, rec_token=rec_token[:n_valid],
                     rec_route=rec_route[:n_valid], route_pos=route_pos,
                     n_valid=int(n_valid))
+
+    def mxfp4_decode(self, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+        """fp32 weights [..., N, K] of MXFP4 codes [..., N, K/2] (two per byte,
+        low nibble first) and E8M0 block scales [..., N, K/32]."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint8)
+        K = codes.shape[-1] * 2
+        assert scales.shape[-1] * 32 == K and scales.shape[:-1] == codes.shape[:-1]
+        N = int(np.prod(codes.shape[:-1]))
+        out = np.empty(codes.shape[:-1] + (K,), dtype=np.float32)
+        self.lib.oracle_mxfp4_decode(N, K, _p(codes), _p(scales), _p(out))
+        return out
 
     def fp8e4m3_decode(self, q: np.ndarray) -> np.ndarray:
         """Values (fp32) of fp8 e4m3 codes (uint8 array of any shape)."""

@@ -392,6 +392,36 @@ def check_fp8_decode(orc):
     assert np.array_equal(got[0x80:0xFF], -got[:0x7F])                  # sign bit negates
 
 
+def check_mxfp4_decode(orc):
+    """MXFP4: every E2M1 code against the OCP table (golden fixture), every
+    E8M0 scale against PyTorch's float8_e8m0fnu conversion (an independent
+    implementation), the nibble order and the 32-wide scale blocks on a
+    hand-made row."""
+    import torch
+    table = np.array(_load("mxfp4_e2m1.json")["e2m1"], dtype=np.float32)
+    # all 16 codes as the low and as the high nibble, scale 2^0
+    codes = np.array([[c | (c << 4) for c in range(16)]], dtype=np.uint8)   # K = 32
+    got = orc.mxfp4_decode(codes, np.array([[127]], dtype=np.uint8))[0]
+    assert np.array_equal(got[0::2].view(np.uint32), table.view(np.uint32))
+    assert np.array_equal(got[1::2].view(np.uint32), table.view(np.uint32))
+    # nibble order: byte 0x21 holds element 0 = code 1 (0.5) and element 1 = code 2 (1.0)
+    row = np.zeros((1, 16), dtype=np.uint8)
+    row[0, 0] = 0x21
+    v = orc.mxfp4_decode(row, np.array([[127]], dtype=np.uint8))[0]
+    assert v[0] == 0.5 and v[1] == 1.0 and np.all(v[2:] == 0.0)
+    # scales: code 2 (1.0) times every E8M0 value; block k // 32 takes scale k // 32
+    sc = np.arange(256, dtype=np.uint8)
+    ones = np.full((256, 16), 0x22, dtype=np.uint8)                         # K = 32, all 1.0
+    got = orc.mxfp4_decode(ones, sc[:, None])[:, 0]
+    ref = torch.from_numpy(sc.copy()).view(torch.float8_e8m0fnu).float().numpy()
+    fin = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(got), ~fin)
+    assert np.array_equal(got[fin].view(np.uint32), ref[fin].view(np.uint32))
+    two = np.full((1, 32), 0x22, dtype=np.uint8)                            # K = 64: two blocks
+    v = orc.mxfp4_decode(two, np.array([[127, 130]], dtype=np.uint8))[0]
+    assert np.all(v[:32] == 1.0) and np.all(v[32:] == 8.0)
+
+
 def check_ffn_row_scales(orc):
     """Weights given as fp8 code values with per-row scales equal the dense
     fp64 brute force on value * scale; unit scales change nothing."""
@@ -439,5 +469,6 @@ ALL_CHECKS = [check_router_golden, check_router_exact_integers, check_router_err
               check_topk_bruteforce, check_topk_special, check_topk_nan_and_signed_zero, check_alpha,
               check_shared,
               check_route_map_golden, check_route_map_bruteforce, check_route_map_errors,
-              check_ffn_dense_bruteforce, check_ffn_special, check_fp8_decode, check_ffn_row_scales,
+              check_ffn_dense_bruteforce, check_ffn_special, check_fp8_decode, check_mxfp4_decode,
+              check_ffn_row_scales,
               check_layer_chain]

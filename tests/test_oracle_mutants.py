@@ -61,6 +61,12 @@ MUTANTS = [
     ("fp8 sign ignored", "out[i] = (float)(sgn ? -v : v);", "out[i] = (float)v;"),
     ("up projection takes the gate scales", "const double scu = Su ? (double)Su[e * f + n] : 1.0;",
      "const double scu = Sg ? (double)Sg[e * f + n] : 1.0;"),
+    ("fp4 nibbles in the wrong order", "(k % 2 == 0) ? (byte & 15) : (byte >> 4)",
+     "(k % 2 == 0) ? (byte >> 4) : (byte & 15)"),
+    ("fp4 exponent bias 0", "ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),
+    ("fp4 subnormal step 1", "e == 0 ? 0.5 * m", "e == 0 ? 1.0 * m"),
+    ("fp4 scale blocks of 16", "scales[n * (K / 32) + k / 32]", "scales[n * (K / 32) + k / 16 % (K / 32)]"),
+    ("fp4 scale bias 128", "ldexp(sgn ? -mag : mag, sc - 127)", "ldexp(sgn ? -mag : mag, sc - 128)"),
     ("down row scale not applied", "(double)wd[m * f + n] * scd * h[n]", "(double)wd[m * f + n] * h[n]"),
 ]
 
