@@ -58,9 +58,13 @@ for _t in (256, 1024, 4096):
         f"32 Mixtral-8x7B-shaped MoE layers with independent weights, all resident (90.2 GB): T={_t}, "
         "d=4096, E=8, top-2 renormalised, SwiGLU f=14336, bf16; only the MoE sublayers are timed")
 for _n in list(WORKLOAD_TEXT):
-    WORKLOAD_TEXT[_n + "_fp8w"] = (WORKLOAD_TEXT[_n].replace(", bf16", ", bf16 activations")
+    _act = WORKLOAD_TEXT[_n].replace("bf16 weights/activations", "bf16").replace(", bf16", ", bf16 activations")
+    WORKLOAD_TEXT[_n + "_fp8w"] = (_act
                                    + "; expert weights stored as fp8 e4m3 codes with one fp32 scale per row "
                                    "(weight-only quantisation, decoded to bf16 MFMA operands)")
+    WORKLOAD_TEXT[_n + "_fp4w"] = (_act
+                                   + "; expert weights stored as MXFP4 (E2M1 codes, one E8M0 scale per 32 "
+                                   "weights of a row; weight-only quantisation, decoded to bf16 MFMA operands)")
 PCIE_GEN5_X16_GBS = 64.0   # one direction, before protocol overhead
 
 
@@ -286,7 +290,9 @@ def torch_bmm_expert_shape(torch, cfg, reps=10) -> dict:
 
 def expert_slice_bytes(cfg) -> int:
     """Bytes of one expert's gate/up and down slices (fp8: codes plus the
-    fp32 row scales)."""
+    fp32 row scales; MXFP4: half a byte a weight plus a scale byte per 32)."""
+    if cfg.fp4_weights:
+        return 3 * cfg.d * cfg.f // 2 + 3 * cfg.d * cfg.f // 32
     if cfg.fp8_weights:
         return 3 * cfg.d * cfg.f + (2 * cfg.f + cfg.d) * 4
     return 3 * cfg.d * cfg.f * (4 if cfg.dtype == "f32" else 2)
@@ -308,6 +314,9 @@ def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
         dec = lambda q: orc.fp8e4m3_decode(q.cpu().numpy())
         Wg, Wu, Wd = dec(inp.Wg), dec(inp.Wu), dec(inp.Wd)
         scales = (f32(inp.Sg), f32(inp.Su), f32(inp.Sd))
+    elif cfg.fp4_weights:   # the oracle decodes the MXFP4 codes and block scales to fp32 weights
+        dec = lambda q, s: orc.mxfp4_decode(q.cpu().numpy(), s.cpu().numpy())
+        Wg, Wu, Wd = dec(inp.Wg, inp.Sg), dec(inp.Wu, inp.Su), dec(inp.Wd, inp.Sd)
     else:
         Wg, Wu, Wd = f32(inp.Wg), f32(inp.Wu), f32(inp.Wd)
     t0 = time.perf_counter()

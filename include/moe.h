@@ -67,6 +67,20 @@ typedef void *moe_stream; /* a hipStream_t */
  * decode the codes to bf16 operands exactly and scale the fp32
  * accumulators. */
 #define MOE_DT_BF16_FP8W 2
+/* bf16 activations; expert weights in OCP MXFP4: 4-bit E2M1 codes (sign, 2
+ * exponent bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6) and one E8M0 scale byte (2^(s-127)) per row and block of 32
+ * weights along K; a weight is code value times its block's scale, which is
+ * exact in bf16. A source slice [N][K] for the packing calls holds the codes
+ * row-major, two per byte (element 2i in the low nibble of byte i), then the
+ * scales [N][K/32]; its size is N*K/2 + N*K/32 bytes. The packed slice in the
+ * arena holds, for each block of 256 rows and each K piece of 32, the rows'
+ * 16 code bytes one row after another, then their scale bytes padded with
+ * zeros to a multiple of 16 (so one K step of a weight tile is one
+ * contiguous run). Strides and slice sizes are in bytes. K (d for gate/up, f
+ * for down) must be a multiple of 32. The expert kernels decode the codes
+ * with their block scales to bf16 operands (exact). */
+#define MOE_DT_BF16_FP4W 3
 
 /* Device error word bits (moe_device_errors). */
 #define MOE_DEVERR_EXPERT_ID 1 /* a top-k id outside [0, E + n_shared) */

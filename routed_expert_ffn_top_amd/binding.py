@@ -26,8 +26,18 @@ MOE_ERR_UNSUPPORTED = -6
 MOE_DT_F32 = 0
 MOE_DT_BF16 = 1
 MOE_DT_BF16_FP8W = 2   # bf16 activations, fp8 e4m3 weights with fp32 row scales
+MOE_DT_BF16_FP4W = 3   # bf16 activations, MXFP4 weights (E2M1 codes, E8M0 scale per 32)
 _DTYPE_CODE = {"f32": MOE_DT_F32, "bf16": MOE_DT_BF16, "bf16_fp8w": MOE_DT_BF16_FP8W,
-               MOE_DT_F32: MOE_DT_F32, MOE_DT_BF16: MOE_DT_BF16, MOE_DT_BF16_FP8W: MOE_DT_BF16_FP8W}
+               "bf16_fp4w": MOE_DT_BF16_FP4W, MOE_DT_F32: MOE_DT_F32, MOE_DT_BF16: MOE_DT_BF16,
+               MOE_DT_BF16_FP8W: MOE_DT_BF16_FP8W, MOE_DT_BF16_FP4W: MOE_DT_BF16_FP4W}
+
+
+def fp4_slice_bytes(N: int, K: int) -> int:
+    """Bytes of a packed MXFP4 slice [N][K]: per 256-row block and 32-wide K
+    piece, 16 code bytes a row plus the rows' scale bytes padded to 16."""
+    piece = lambda rows: rows * 16 + (rows + 15) // 16 * 16
+    full, rem = divmod(N, 256)
+    return (K // 32) * (full * piece(256) + (piece(rem) if rem else 0))
 MOE_DEVERR_EXPERT_ID = 1
 MOE_ROUTE_RESET = 1
 MOE_FFN_EXPERTS = 1
@@ -308,10 +318,14 @@ class Arena:
 
     def __init__(self, shape: moe_shape, G: Optional[int] = None, device="cuda"):
         self.shape = shape
-        if shape.dtype == MOE_DT_BF16_FP8W:
-            # a slice is its codes then its row scales; strides in bytes
-            self.stride_gu = 2 * shape.f * shape.d + 8 * shape.f
-            self.stride_d = shape.d * shape.f + 4 * shape.d
+        if shape.dtype in (MOE_DT_BF16_FP8W, MOE_DT_BF16_FP4W):
+            # a slice is its codes then its scales; strides in bytes
+            if shape.dtype == MOE_DT_BF16_FP8W:
+                self.stride_gu = 2 * shape.f * shape.d + 8 * shape.f
+                self.stride_d = shape.d * shape.f + 4 * shape.d
+            else:
+                self.stride_gu = fp4_slice_bytes(2 * shape.f, shape.d)
+                self.stride_d = fp4_slice_bytes(shape.d, shape.f)
             self.plane_gu = torch.empty((shape.P, self.stride_gu), dtype=torch.uint8, device=device)
             self.plane_d = torch.empty((shape.P, self.stride_d), dtype=torch.uint8, device=device)
         else:
@@ -337,7 +351,7 @@ class Arena:
 
     def load_resident(self, Wg, Wu, Wd, phi: Sequence[int], stream=None, scales=None):
         """Pack and publish every expert e with phi[e] >= 0 into slot phi[e].
-        scales: (Sg, Su, Sd) row scales when the weights are fp8 codes."""
+        scales: (Sg, Su, Sd) row scales (fp8 codes) or block scales (MXFP4)."""
         for e, s in enumerate(phi):
             if s < 0:
                 continue
@@ -349,11 +363,12 @@ class Arena:
 
 def expert_slices(Wg, Wu, Wd, scales, e):
     """Expert e's gate, up and down slices in the layout the C ABI takes:
-    the weight rows, then (fp8 codes) the rows' fp32 scales as bytes."""
+    the weight rows, then (fp8 codes) the rows' fp32 scales as bytes or
+    (MXFP4: packed code bytes [N][K/2]) the E8M0 scale bytes [N][K/32]."""
     if scales is None:
         return Wg[e], Wu[e], Wd[e]
     Sg, Su, Sd = scales
-    cat = lambda q, sc: torch.cat([q[e].reshape(-1), sc[e].contiguous().view(torch.uint8)])
+    cat = lambda q, sc: torch.cat([q[e].reshape(-1), sc[e].contiguous().view(torch.uint8).reshape(-1)])
     return cat(Wg, Sg), cat(Wu, Su), cat(Wd, Sd)
 
 

@@ -72,8 +72,9 @@ moe_status check_shape(const moe_shape *s)
     if (s->k + s->n_shared > 64) return fail(MOE_ERR_UNSUPPORTED, "k + n_shared must be <= 64");
     if (s->P < 1 || s->P > kMaxExp) return fail(MOE_ERR_INVALID_ARG, "need 1 <= P <= %d", kMaxExp);
     if (s->capacity < 1) return fail(MOE_ERR_INVALID_ARG, "capacity must be >= 1");
-    if (s->dtype != MOE_DT_BF16 && s->dtype != MOE_DT_F32 && s->dtype != MOE_DT_BF16_FP8W)
-        return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_DT_BF16, MOE_DT_BF16_FP8W or MOE_DT_F32");
+    if (s->dtype != MOE_DT_BF16 && s->dtype != MOE_DT_F32 && s->dtype != MOE_DT_BF16_FP8W &&
+        s->dtype != MOE_DT_BF16_FP4W)
+        return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_DT_BF16, MOE_DT_BF16_FP8W, MOE_DT_BF16_FP4W or MOE_DT_F32");
     if (s->ldx < s->d || s->ldy < s->d || (s->ldy % 4) != 0)
         return fail(MOE_ERR_INVALID_ARG, "need ldx >= d, ldy >= d, ldy %% 4 == 0");
     if ((s->d % 4) != 0) return fail(MOE_ERR_UNSUPPORTED, "d must be a multiple of 4");
@@ -390,7 +391,7 @@ GemmArgs gemm_args(const moe_shape &s, const moe_routes &r, const moe_arena *a)
 moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, const moe_routes &r,
                         moe_arena *a, int max_rows, bool simple, void *ws, hipStream_t st)
 {
-    if (simple && w_fp8(s))
+    if (simple && (w_fp8(s) || w_fp4(s)))
         return fail(MOE_ERR_UNSUPPORTED, "the plain kernel reads bf16 or fp32 weights only");
     GemmArgs g = gemm_args(s, r, a);
     g.A = X;
@@ -398,6 +399,7 @@ moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, co
     g.B = a->plane_gu;
     g.slot_stride = a->stride_gu;
     g.bfp8 = w_fp8(s);
+    g.bfp4 = w_fp4(s);
     g.scale_off = (int64_t)2 * s.f * s.d;   // fp8: the row scales follow the codes
     g.N = 2 * s.f;
     g.K = s.d;
@@ -410,6 +412,7 @@ moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, co
     h.B = a->plane_d;
     h.slot_stride = a->stride_d;
     h.bfp8 = w_fp8(s);
+    h.bfp4 = w_fp4(s);
     h.scale_off = (int64_t)s.d * s.f;
     h.N = s.d;
     h.K = s.f;
@@ -541,7 +544,7 @@ moe_status moe_pack_gate_up(const moe_shape *shape, const void *W_g, const void 
     MOE_TRY(check_shape(shape));
     if (!W_g || !W_u || !dst || n < 0) return fail(MOE_ERR_INVALID_ARG, "pack: bad arguments");
     const int esz = w_esz(*shape);
-    const size_t src_bytes = (size_t)shape->f * shape->d * esz + (w_fp8(*shape) ? (size_t)shape->f * 4 : 0);
+    const size_t src_bytes = src_slice_bytes(*shape, shape->f, shape->d);
     if (n > 1 && ((size_t)src_stride * esz < src_bytes || (size_t)dst_stride * esz < gu_slice_bytes(*shape)))
         return fail(MOE_ERR_INVALID_ARG, "pack: strides smaller than a slice");
     if (((src_stride * esz) % 4) != 0 || ((dst_stride * esz) % 4) != 0)
@@ -550,10 +553,35 @@ moe_status moe_pack_gate_up(const moe_shape *shape, const void *W_g, const void 
     return MOE_OK;
 }
 
+// MXFP4: source row sr of a source slice with Nsrc rows (codes [Nsrc][K/2],
+// then scales [Nsrc][K/32]) into row r of the packed [N][K] slice at dst.
+static void fp4_pack_row_host(const uint8_t *src, int64_t Nsrc, int64_t sr, uint8_t *dst, int64_t N, int64_t K,
+                              int64_t r)
+{
+    const int64_t b = r / kWRows, rb = r % kWRows, rows = std::min<int64_t>(kWRows, N - b * kWRows);
+    uint8_t *base = dst + b * (K / kWK) * fp4_piece_bytes(kWRows);
+    const uint8_t *codes = src + sr * (K / 2), *sc = src + Nsrc * (K / 2) + sr * (K / kWK);
+    for (int64_t p = 0; p < K / kWK; ++p) {
+        uint8_t *piece = base + p * fp4_piece_bytes(rows);
+        memcpy(piece + rb * 16, codes + p * 16, 16);
+        piece[rows * 16 + rb] = sc[p];
+        if (rb == rows - 1) memset(piece + rows * 17, 0, (size_t)(fp4_piece_bytes(rows) - rows * 17));
+    }
+}
+
 moe_status moe_pack_gate_up_host(const moe_shape *shape, const void *W_g, const void *W_u, void *dst)
 {
     MOE_TRY(check_shape(shape));
     if (!W_g || !W_u || !dst) return fail(MOE_ERR_INVALID_ARG, "pack: NULL pointer");
+    if (w_fp4(*shape)) {
+        const int f = shape->f;
+        for (int r = 0; r < 2 * f; ++r) {
+            const int q = r / 64, w = r % 64;
+            const int sr = w < 32 ? 32 * q + w : 32 * q + w - 32;
+            fp4_pack_row_host((const uint8_t *)(w < 32 ? W_g : W_u), f, sr, (uint8_t *)dst, 2 * f, shape->d, r);
+        }
+        return MOE_OK;
+    }
     const size_t esz = (size_t)w_esz(*shape);
     const size_t row = (size_t)shape->d * esz;
     const int f = shape->f, d = shape->d;
@@ -576,7 +604,8 @@ moe_status moe_pack_down(const moe_shape *shape, const void *W_d, void *dst, int
     MOE_TRY(check_shape(shape));
     if (!W_d || !dst || n < 0) return fail(MOE_ERR_INVALID_ARG, "pack: bad arguments");
     const int esz = w_esz(*shape);
-    if (n > 1 && ((size_t)src_stride * esz < d_slice_bytes(*shape) || (size_t)dst_stride * esz < d_slice_bytes(*shape)))
+    if (n > 1 && ((size_t)src_stride * esz < src_slice_bytes(*shape, shape->d, shape->f) ||
+                  (size_t)dst_stride * esz < d_slice_bytes(*shape)))
         return fail(MOE_ERR_INVALID_ARG, "pack: strides smaller than a slice");
     if (((src_stride * esz) % 4) != 0 || ((dst_stride * esz) % 4) != 0)
         return fail(MOE_ERR_INVALID_ARG, "pack: strides must be whole 32-bit words");
@@ -588,6 +617,11 @@ moe_status moe_pack_down_host(const moe_shape *shape, const void *W_d, void *dst
 {
     MOE_TRY(check_shape(shape));
     if (!W_d || !dst) return fail(MOE_ERR_INVALID_ARG, "pack: NULL pointer");
+    if (w_fp4(*shape)) {
+        for (int m = 0; m < shape->d; ++m)
+            fp4_pack_row_host((const uint8_t *)W_d, shape->d, m, (uint8_t *)dst, shape->d, shape->f, m);
+        return MOE_OK;
+    }
     const size_t esz = (size_t)w_esz(*shape);
     const int d = shape->d, f = shape->f;
     for (int m = 0; m < d; ++m)

@@ -110,6 +110,40 @@ __global__ __launch_bounds__(256) void k_pack_down(const uint32_t *__restrict__ 
     if (scale_w > 0 && threadIdx.x == 0) out[scale_w + m] = slice[scale_w + m];
 }
 
+// MXFP4 packing: source row sr of expert e's source slice (codes
+// [Nsrc][K/2], then scales [Nsrc][K/32]) to row r of the packed [N][K] slice:
+// in each K piece of its 256-row block, its 16 code bytes at row r % 256 and
+// its scale byte after the block's codes; the last row of a block zeroes the
+// piece's padding. gateup: r is a packed gate/up row (interleaved from Wg
+// and Wu), else a down row of Wg. Sources and destinations 4-byte aligned.
+__global__ __launch_bounds__(64) void k_pack_fp4(const uint8_t *__restrict__ Wg, const uint8_t *__restrict__ Wu,
+                                                 uint8_t *__restrict__ dst, int64_t src_stride, int64_t dst_stride,
+                                                 int Nsrc, int N, int K, int gateup)
+{
+    const int r = blockIdx.x, e = blockIdx.y;
+    int sr = r;
+    const uint8_t *slice = Wg + (int64_t)e * src_stride;
+    if (gateup) {
+        const int q = r >> 6, w = r & 63;
+        sr = w < 32 ? 32 * q + w : 32 * q + w - 32;
+        slice = (w < 32 ? Wg : Wu) + (int64_t)e * src_stride;
+    }
+    const int b = r / kWRows, rb = r % kWRows, rows = min(kWRows, N - b * kWRows);
+    uint8_t *base = dst + (int64_t)e * dst_stride + (int64_t)b * (K / kWK) * fp4_piece_bytes(kWRows);
+    const uint8_t *codes = slice + (int64_t)sr * (K / 2);
+    const uint8_t *sc = slice + (int64_t)Nsrc * (K / 2) + (int64_t)sr * (K / kWK);
+    for (int p = threadIdx.x; p < K / kWK; p += 64) {
+        uint8_t *piece = base + (int64_t)p * fp4_piece_bytes(rows);
+        const uint32_t *cs = (const uint32_t *)(codes + p * 16);
+        uint32_t *cd = (uint32_t *)(piece + rb * 16);
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) cd[w4] = cs[w4];
+        piece[rows * 16 + rb] = sc[p];
+        if (rb == rows - 1)
+            for (int64_t z = (int64_t)rows * 17; z < fp4_piece_bytes(rows); ++z) piece[z] = 0;
+    }
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -167,6 +201,11 @@ hipError_t launch_pack_gate_up(const moe_shape &s, const void *Wg, const void *W
                                int n, int64_t src_stride, int64_t dst_stride, hipStream_t st)
 {
     if (n == 0) return hipSuccess;
+    if (w_fp4(s)) {
+        hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)(2 * s.f), (unsigned)n), dim3(64), 0, st, (const uint8_t *)Wg,
+                           (const uint8_t *)Wu, (uint8_t *)dst, src_stride, dst_stride, s.f, 2 * s.f, s.d, 1);
+        return hipGetLastError();
+    }
     const int esz = w_esz(s);
     const int64_t row_words = (int64_t)s.d * esz / 4;
     const int64_t ssw = src_stride * esz / 4, dsw = dst_stride * esz / 4;
@@ -183,6 +222,11 @@ hipError_t launch_pack_down(const moe_shape &s, const void *Wd, void *dst, int n
                             int64_t dst_stride, hipStream_t st)
 {
     if (n == 0) return hipSuccess;
+    if (w_fp4(s)) {
+        hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)s.d, (unsigned)n), dim3(64), 0, st, (const uint8_t *)Wd,
+                           (const uint8_t *)nullptr, (uint8_t *)dst, src_stride, dst_stride, s.d, s.d, s.f, 0);
+        return hipGetLastError();
+    }
     const int esz = w_esz(s);
     const int64_t row_words = (int64_t)s.f * esz / 4;
     const int64_t ssw = src_stride * esz / 4, dsw = dst_stride * esz / 4;

@@ -35,19 +35,16 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Element formats. MOE_DT_BF16_FP8W: bf16 activations, fp8 e4m3 expert
 // weights with one fp32 scale per weight row (a slot slice holds the codes,
-// then the scales).
-inline bool act_bf16(const moe_shape &s) { return s.dtype == MOE_DT_BF16 || s.dtype == MOE_DT_BF16_FP8W; }
+// then the scales). MOE_DT_BF16_FP4W: bf16 activations, MXFP4 expert
+// weights (E2M1 codes, one E8M0 scale per 32 weights of a row). With
+// quantised weights, slice sizes and strides are in bytes (w_esz == 1).
+inline bool act_bf16(const moe_shape &s)
+{
+    return s.dtype == MOE_DT_BF16 || s.dtype == MOE_DT_BF16_FP8W || s.dtype == MOE_DT_BF16_FP4W;
+}
 inline bool w_fp8(const moe_shape &s) { return s.dtype == MOE_DT_BF16_FP8W; }
+inline bool w_fp4(const moe_shape &s) { return s.dtype == MOE_DT_BF16_FP4W; }
 inline int w_esz(const moe_shape &s) { return s.dtype == MOE_DT_F32 ? 4 : (s.dtype == MOE_DT_BF16 ? 2 : 1); }
-// bytes of one expert's packed gate/up slice and down slice (codes + scales for fp8)
-inline size_t gu_slice_bytes(const moe_shape &s)
-{
-    return (size_t)2 * s.f * s.d * w_esz(s) + (w_fp8(s) ? (size_t)2 * s.f * 4 : 0);
-}
-inline size_t d_slice_bytes(const moe_shape &s)
-{
-    return (size_t)s.d * s.f * w_esz(s) + (w_fp8(s) ? (size_t)s.d * 4 : 0);
-}
 
 // Tiled layout of an expert weight slice [N][K] in the arena (section 3.3:
 // weights are stored offline in the order the kernels consume them). Rows
@@ -66,6 +63,35 @@ __host__ __device__ inline int64_t wtile_off(int64_t n, int64_t k, int64_t N, in
     const int64_t rows = N - nb * kWRows < kWRows ? N - nb * kWRows : kWRows;
     const int64_t w = K - kp * kWK < kWK ? K - kp * kWK : kWK;
     return nb * kWRows * K + kp * rows * kWK + (n % kWRows) * w + k % kWK;
+}
+
+// Packed MXFP4 slice [N][K]: for each 256-row block and each 32-wide K piece,
+// the block's rows' 16 code bytes one row after another, then the rows'
+// scale bytes padded with zeros to a multiple of 16. One K step of a weight
+// tile is again one contiguous run (rows*16 + align16(rows) bytes).
+__host__ __device__ inline int64_t fp4_piece_bytes(int64_t rows) { return rows * 16 + (rows + 15) / 16 * 16; }
+inline int64_t fp4_slice_bytes(int64_t N, int64_t K)
+{
+    const int64_t full = N / kWRows, rem = N % kWRows;
+    return (K / kWK) * (full * fp4_piece_bytes(kWRows) + (rem ? fp4_piece_bytes(rem) : 0));
+}
+// bytes of one expert's packed gate/up slice and down slice (codes + scales
+// for the quantised formats)
+inline size_t gu_slice_bytes(const moe_shape &s)
+{
+    if (w_fp4(s)) return (size_t)fp4_slice_bytes(2 * (int64_t)s.f, s.d);
+    return (size_t)2 * s.f * s.d * w_esz(s) + (w_fp8(s) ? (size_t)2 * s.f * 4 : 0);
+}
+inline size_t d_slice_bytes(const moe_shape &s)
+{
+    if (w_fp4(s)) return (size_t)fp4_slice_bytes(s.d, s.f);
+    return (size_t)s.d * s.f * w_esz(s) + (w_fp8(s) ? (size_t)s.d * 4 : 0);
+}
+// bytes of one unpacked source slice [N][K] handed to the packing calls
+inline size_t src_slice_bytes(const moe_shape &s, int64_t N, int64_t K)
+{
+    if (w_fp4(s)) return (size_t)(N * K / 2 + N * K / 32);
+    return (size_t)(N * K * w_esz(s)) + (w_fp8(s) ? (size_t)N * 4 : 0);
 }
 
 // Splits of the down projection's K = f: when the down tiles (about
@@ -117,6 +143,7 @@ struct GemmArgs {
     const void *B;               // plane base
     int64_t slot_stride;         // elements (bytes for fp8 weights)
     int bfp8;                    // B: fp8 e4m3 codes with fp32 row scales
+    int bfp4;                    // B: packed MXFP4 slice (codes and block scales per K piece)
     int64_t scale_off;           // fp8: bytes from a slot slice's start to its row scales
     int N, K;
     void *C;                     // H (gate/up) or Yr (down)

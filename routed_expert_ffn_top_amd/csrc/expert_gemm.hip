@@ -209,24 +209,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // B rows then take 32 bytes per stage; each wave's fragments are converted to
 // bf16 (exactly: every e4m3 value is a bf16 value) just before its MFMAs, and
 // the row scales multiply the fp32 accumulators in the epilogue.
+// BF4: the weights (B) are a packed MXFP4 slice. A stage of B holds the tile's
+// 256 rows x 16 code bytes (one K piece of 32 weights per row) and the rows'
+// 256 E8M0 scale bytes; waves 0-3 copy 1 KB of codes each, waves 4-7 64 B
+// of scales each, so every wave issues the same number of copies. A wave
+// reads 8 codes (4 bytes) and the row's scale per fragment and decodes them
+// with v_cvt_scalef32_pk_bf16_fp4 (code value x power-of-two scale: exact in
+// bf16) just before its MFMAs; the epilogue applies no scale.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w, float scale)
+{
+    typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+    const u32x4v_t u = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+// E8M0 scale byte -> fp32: 2^(s-127); s = 0 is the subnormal 2^-127, s = 255 NaN
+__device__ __forceinline__ float e8m0_to_f32(uint32_t sb)
+{
+    return __uint_as_float(sb == 0 ? 0x00400000u : (sb == 255 ? 0x7fc00000u : sb << 23));
+}
+
 #ifndef MOE_GEMM_MAX_SLOTS
 #define MOE_GEMM_MAX_SLOTS kMaxExp
 #endif
 constexpr int kGemmMaxSlots = MOE_GEMM_MAX_SLOTS;
 
-template <int BM, int BN, int NS, int WM, int WN, bool GATEUP, bool BF8>
+template <int BM, int BN, int NS, int WM, int WN, bool GATEUP, bool BF8, bool BF4 = false>
 __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
 {
     constexpr int NW = WM * WN, NT = NW * 64;
     constexpr int BK = 32, ROWB = 64;                   // bytes per LDS row of A (32 bf16)
-    constexpr int BROW = BF8 ? 32 : 64;                 // bytes per LDS row of B (32 codes or 32 bf16)
-    constexpr int BESZ = BF8 ? 1 : 2;                   // bytes per B element
+    constexpr int BROW = BF8 ? 32 : (BF4 ? 16 : 64);    // bytes per LDS row of B (32 codes or 32 bf16)
+    constexpr int BESZ = (BF8 || BF4) ? 1 : 2;          // bytes per B element (B strides in bytes when 1)
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int MI = TM / 32, NI = TN / 32;
-    constexpr int STAGE = BM * ROWB + BN * BROW;        // bytes per stage
-    constexpr int AI = BM / 16 / NW, BI = BN * BROW / 1024 / NW; // 1 KB copies per wave per stage
+    constexpr int STAGE = BM * ROWB + BN * BROW + (BF4 ? BN : 0);   // bytes per stage (BF4: + scales)
+    constexpr int AI = BM / 16 / NW, BI = BF4 ? 1 : BN * BROW / 1024 / NW; // copies per wave per stage
     constexpr int LOADS = AI + BI;
-    static_assert(BM % (16 * NW) == 0 && (BN * BROW) % (1024 * NW) == 0 && MI >= 1 && NI >= 1, "tile");
+    static_assert(BM % (16 * NW) == 0 && (BF4 || (BN * BROW) % (1024 * NW) == 0) && MI >= 1 && NI >= 1, "tile");
+    static_assert(!BF4 || (NW == 8 && BN == 256), "MXFP4 copies: 4 waves of codes, 4 of scales");
+    static_assert(!(BF8 && BF4), "one weight format");
     static_assert(!GATEUP || (TN % 64) == 0, "gate/up pairs need 64-column wave tiles");
     static_assert(NS >= 3, "the ring needs at least 3 stages");
     static_assert(BK == kWK && kWRows % BN == 0, "a B stage is one K piece of one row block of the tiled layout");
@@ -336,6 +360,20 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         const char *Bslot = (const char *)a.B + (int64_t)t.slot * a.slot_stride * BESZ;
         const int nb = t.n0 / kWRows;
         const int rows_nb = min(kWRows, N - nb * kWRows);
+        if constexpr (BF4) {
+            // MXFP4 pieces: rows_nb * 16 code bytes, then the padded scale bytes
+            const int64_t piece = fp4_piece_bytes(rows_nb);
+            bstep = (int)piece;
+            const char *Bblk = Bslot + (int64_t)nb * (K / BK) * fp4_piece_bytes(kWRows) + (int64_t)(t.ks * Kc / BK) * piece;
+            if (wave < 4) {
+                const int n = min(t.n0 + wave * 64 + lane, N - 1);
+                bsrc[0] = Bblk + (int64_t)(n - nb * kWRows) * 16;
+            } else {
+                const int off = (wave - 4) * 64 + lane * 16;   // lanes 0-3 copy
+                bsrc[0] = Bblk + (int64_t)rows_nb * 16 + (off + 16 <= (int)(piece - rows_nb * 16) ? off : 0);
+            }
+            return;
+        }
         bstep = rows_nb * BK * BESZ;
         const char *Bblk = Bslot + ((int64_t)nb * kWRows * K + (int64_t)(t.ks * Kc / BK) * rows_nb * BK) * BESZ;
 #pragma unroll
@@ -388,11 +426,19 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         for (int j = 0; j < AI; ++j)
             __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(asrc[j] + kb),
                                              (LDS_AS void *)(st + (wave * AI + j) * 1024), 16, 0, 0);
+        if constexpr (BF4) {
+            // waves 0-3: 64 rows of 16 code bytes; waves 4-7: lanes 0-3 copy 64 scale bytes
+            if (wave < 4 || lane < 4)
+                __builtin_amdgcn_global_load_lds(
+                    (const GLOBAL_AS void *)(bsrc[0] + (int64_t)kt * bstep),
+                    (LDS_AS void *)(st + BM * ROWB + (wave < 4 ? wave * 1024 : BN * 16 + (wave - 4) * 64)), 16, 0, 0);
+        } else {
 #pragma unroll
-        for (int j = 0; j < BI; ++j)
-            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(bsrc[j] + (int64_t)kt * bstep),
-                                             (LDS_AS void *)(st + BM * ROWB + (wave * BI + j) * 1024), 16, 0,
-                                             0);
+            for (int j = 0; j < BI; ++j)
+                __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(bsrc[j] + (int64_t)kt * bstep),
+                                                 (LDS_AS void *)(st + BM * ROWB + (wave * BI + j) * 1024), 16, 0,
+                                                 0);
+        }
     };
 
     // fragment addressing: row (lane & 31) of each 32-row tile, logical chunk
@@ -403,6 +449,8 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     f32x16_t acc[MI][NI];
     bf16x8_t af[2][MI], bfr[2][NI];
     u32x2_t braw[2][NI];   // fp8 weights: 8 codes per fragment, converted in mfmas
+    uint32_t b4raw[2][NI], b4sc[2][NI];   // MXFP4: 8 codes and the row's scale byte per fragment
+    const int c4[2] = {(0 + (lane >> 5)) * 4, (2 + (lane >> 5)) * 4};   // code bytes of chunk 2*ks + (lane >> 5)
     // fp8 fragment of B row (lane & 31): 8-byte piece c = 2*ks + (lane >> 5) of
     // the 32-byte row, stored in 16-byte half (c >> 1) ^ ((row >> 3) & 1)
     const int br8 = lane & 31;
@@ -416,6 +464,14 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
             const char *Bs = lds + stage * STAGE + BM * ROWB + wn * TN * BROW + boff8[ks];
 #pragma unroll
             for (int j = 0; j < NI; ++j) braw[set][j] = *(const u32x2_t *)(Bs + j * 32 * BROW);
+        } else if constexpr (BF4) {
+            const char *Bs = lds + stage * STAGE + BM * ROWB;
+            const int r0 = wn * TN + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                b4raw[set][j] = *(const uint32_t *)(Bs + (r0 + j * 32) * 16 + c4[ks]);
+                b4sc[set][j] = *(const uint8_t *)(Bs + BN * 16 + r0 + j * 32);
+            }
         } else {
             const char *Bs = lds + stage * STAGE + BM * ROWB + wn * TN * ROWB + foff[ks];
 #pragma unroll
@@ -427,6 +483,10 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
 #pragma unroll
             for (int j = 0; j < NI; ++j) bfr[set][j] = fp8x8_to_bf16(braw[set][j]);
         }
+        if constexpr (BF4) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) bfr[set][j] = fp4x8_to_bf16(b4raw[set][j], e8m0_to_f32(b4sc[set][j]));
+        }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -435,13 +495,15 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     };
     // interleave: the (MI + NI) fragment reads of the next step are spread
     // over the MI * NI MFMAs of this step
+    constexpr int NRD = MI + (BF4 ? 2 : 1) * NI;   // LDS reads per step (BF4: codes and scale)
     auto interleave = [&]() {
 #pragma unroll
-        for (int q = 0; q < MI + NI; ++q) {
+        for (int q = 0; q < (NRD < MI * NI ? NRD : MI * NI); ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
+        if constexpr (MI * NI > NRD) __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - NRD, 0);
+        if constexpr (NRD > MI * NI) __builtin_amdgcn_sched_group_barrier(0x100, NRD - MI * NI, 0);
     };
 
     const int nk = Kc / BK;
@@ -750,8 +812,9 @@ hipError_t launch_mfma_lds(const GemmArgs &a, int max_rows, hipStream_t st)
     // compute unit when the LDS ring fills it), never more than there can be
     // tiles
     if (a.P > kGemmMaxSlots) return hipErrorInvalidValue;   // the slot tables live in LDS
-    auto kern = a.bfp8 ? (const void *)k_gemm_mfma_lds<BM, BN, MOE_FP8_STAGES_OF(NS), WM, WN, GATEUP, true>
-                       : (const void *)k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, false>;
+    auto kern = a.bfp8   ? (const void *)k_gemm_mfma_lds<BM, BN, MOE_FP8_STAGES_OF(NS), WM, WN, GATEUP, true>
+                : a.bfp4 ? (const void *)k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, false, true>
+                         : (const void *)k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, false>;
     int per_cu = 1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WM * WN * 64, 0) != hipSuccess || per_cu < 1)
         per_cu = 1;
@@ -759,6 +822,9 @@ hipError_t launch_mfma_lds(const GemmArgs &a, int max_rows, hipStream_t st)
     if (g == 0) return hipSuccess;
     if (a.bfp8)
         hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, MOE_FP8_STAGES_OF(NS), WM, WN, GATEUP, true>), dim3(g),
+                           dim3(WM * WN * 64), 0, st, a);
+    else if (a.bfp4)
+        hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, false, true>), dim3(g),
                            dim3(WM * WN * 64), 0, st, a);
     else
         hipLaunchKernelGGL((k_gemm_mfma_lds<BM, BN, NS, WM, WN, GATEUP, false>), dim3(g), dim3(WM * WN * 64), 0,
@@ -793,7 +859,7 @@ hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, b
     if (max_rows == 0) return hipSuccess;
     if (s.dtype == MOE_DT_F32) return launch_simple<float, true>(a, max_rows, st);
     if (simple) {
-        if (a.bfp8) return hipErrorInvalidValue;   // the plain kernel reads bf16 weights only
+        if (a.bfp8 || a.bfp4) return hipErrorInvalidValue;   // the plain kernel reads bf16 weights only
         return launch_simple<uint16_t, true>(a, max_rows, st);
     }
     return launch_mfma_lds<MOE_RING_TILE, true>(a, max_rows, st);
@@ -805,7 +871,7 @@ hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool
     if (max_rows == 0) return hipSuccess;
     if (s.dtype == MOE_DT_F32) return launch_simple<float, false>(a, max_rows, st);
     if (simple) {
-        if (a.bfp8) return hipErrorInvalidValue;
+        if (a.bfp8 || a.bfp4) return hipErrorInvalidValue;
         return launch_simple<uint16_t, false>(a, max_rows, st);
     }
     return launch_mfma_lds<MOE_DOWN_TILE, false>(a, max_rows, st);

@@ -33,6 +33,15 @@ codes and one fp32 scale, scale = max|row| / 448 (the largest e4m3 value),
 codes = row / scale rounded to nearest even by PyTorch's float8_e4m3fn
 conversion. The quantised model is then the model under test: both sides get
 the codes and the scales.
+
+MXFP4 workloads (dtype ``bf16_fp4w``, names ending in ``_fp4w``): the same
+fp32 weight draws in the OCP microscaling format, per row and block of 32
+weights along the input dimension: shared exponent
+s = floor(log2(max|block|)) - 2 (2 is the exponent of 6, the largest E2M1
+value), clamped to [-127, 127] and stored as the byte s + 127; each weight
+w / 2^s rounded to the nearest E2M1 value (ties to the even code), values
+beyond 6 saturated to 6; an all-zero block gets s = -127. Codes are stored
+two per byte, element 2i in the low nibble.
 """
 from __future__ import annotations
 
@@ -54,8 +63,9 @@ class MoEConfig:
     k: int
     f: int
     n_shared: int = 0
-    dtype: str = "bf16"          # "bf16", "f32" (X, expert weights, H), or "bf16_fp8w"
+    dtype: str = "bf16"          # "bf16", "f32" (X, expert weights, H), "bf16_fp8w"
                                  # (bf16 X and H, fp8 e4m3 weights with row scales)
+                                 # or "bf16_fp4w" (bf16 X and H, MXFP4 weights)
     renorm: bool = True          # renormalise the top-k softmax weights
     zipf: bool = False           # Zipf(1.1) popularity bias on the logits
     P: Optional[int] = None      # arena slots (None: one slot per expert)
@@ -83,6 +93,15 @@ class MoEConfig:
     @property
     def fp8_weights(self) -> bool:
         return self.dtype == "bf16_fp8w"
+
+    @property
+    def fp4_weights(self) -> bool:
+        return self.dtype == "bf16_fp4w"
+
+    @property
+    def quant_weights(self) -> bool:
+        """Weights stored as codes plus scales (fp8 rows or MXFP4 blocks)."""
+        return self.fp8_weights or self.fp4_weights
 
     def with_(self, **kw) -> "MoEConfig":
         return dataclasses.replace(self, **kw)
@@ -117,6 +136,7 @@ for _t in (256, 512, 1024, 2048, 4096):
 for _n in ("olmoe_t1024", "olmoe_t4096", "dsv2lite_t4096", "mixtral_t256", "mixtral_t1024",
            "mixtral_t4096", "virt_olmoe_t256", "virt_olmoe_t1024", "virt_olmoe_t4096"):
     CONFIGS[_n + "_fp8w"] = CONFIGS[_n].with_(name=_n + "_fp8w", dtype="bf16_fp8w")
+    CONFIGS[_n + "_fp4w"] = CONFIGS[_n].with_(name=_n + "_fp4w", dtype="bf16_fp4w")
 
 
 def seed_for(cfg: MoEConfig, layer: int = 0) -> int:
@@ -134,6 +154,8 @@ class LayerInputs:
     Wd: torch.Tensor              # [n_exp, d, f] cfg dtype
     A: torch.Tensor               # [T, d]        fp32 residual
     # fp8 weights: Wg, Wu, Wd hold e4m3 codes (uint8) and these the row scales
+    # MXFP4: Wg, Wu [n_exp, f, d/2], Wd [n_exp, d, f/2] hold packed E2M1 codes
+    # (uint8) and these the E8M0 block scale bytes (uint8 [..., rows, K/32])
     Sg: Optional[torch.Tensor] = None   # [n_exp, f] fp32
     Su: Optional[torch.Tensor] = None   # [n_exp, f] fp32
     Sd: Optional[torch.Tensor] = None   # [n_exp, d] fp32
@@ -157,6 +179,39 @@ def quantize_rows_e4m3(W: torch.Tensor):
     scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).to(torch.float32)
     codes = (W / scale.unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8)
     return codes, scale
+
+
+# E2M1 magnitudes by code (bit 3 is the sign)
+E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def quantize_mxfp4(W: torch.Tensor):
+    """MXFP4 storage of W [..., rows, K] (fp32, K a multiple of 32): returns
+    (codes uint8 [..., rows, K/2], two E2M1 codes per byte with element 2i in
+    the low nibble; scales uint8 [..., rows, K/32], E8M0 bytes)."""
+    *lead, rows, K = W.shape
+    Wb = W.reshape(*lead, rows, K // 32, 32).to(torch.float32)
+    amax = Wb.abs().amax(dim=-1)
+    # floor(log2 amax) exactly: frexp gives amax = m * 2^e with m in [0.5, 1)
+    _, e = torch.frexp(amax)
+    s = torch.where(amax > 0, e.to(torch.int32) - 1 - 2, torch.full_like(e, -127, dtype=torch.int32))
+    s = s.clamp(-127, 127)
+    v = (Wb / torch.ldexp(torch.ones_like(amax), s.to(torch.float32)).unsqueeze(-1)).abs()
+    # nearest E2M1 magnitude, ties to the even code (midpoints between
+    # neighbouring values go to the one whose code is even)
+    grid = torch.tensor(E2M1_VALUES, dtype=torch.float32, device=W.device)
+    dist = (v.unsqueeze(-1) - grid).abs()
+    best = dist.min(dim=-1, keepdim=True).values
+    cand = (dist == best)
+    codes_idx = torch.arange(8, device=W.device)
+    # among tied candidates prefer the even code
+    pref = torch.where(cand, (codes_idx % 2) * 16 + codes_idx, torch.full_like(codes_idx, 99))
+    mag = pref.min(dim=-1).values % 16
+    mag = torch.where(v >= 6.0, torch.full_like(mag, 7), mag)
+    sign = (Wb < 0) & (mag > 0)
+    code = (mag + 8 * sign.to(mag.dtype)).to(torch.uint8).reshape(*lead, rows, K)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous(), (s + 127).to(torch.uint8).contiguous()
 
 
 def _normal(gen, shape, std, device):
@@ -190,6 +245,8 @@ def make_inputs(cfg: MoEConfig, layer: int = 0, device="cpu",
     Sg = Su = Sd = None
     if cfg.fp8_weights:
         (Wg, Sg), (Wu, Su), (Wd, Sd) = (quantize_rows_e4m3(w) for w in (Wg, Wu, Wd))
+    elif cfg.fp4_weights:
+        (Wg, Sg), (Wu, Su), (Wd, Sd) = (quantize_mxfp4(w) for w in (Wg, Wu, Wd))
     else:
         Wg, Wu, Wd = Wg.to(dt), Wu.to(dt), Wd.to(dt)
     if residual:
@@ -234,5 +291,6 @@ def rows_per_slot_stats(counts) -> dict:
 
 
 __all__ = ["MoEConfig", "CONFIGS", "LayerInputs", "make_inputs", "make_logits", "quantize_rows_e4m3",
+           "quantize_mxfp4", "E2M1_VALUES",
            "seed_for", "identity_phi", "random_phi", "zipf_bias", "STD_W",
            "rows_per_slot_stats"]

@@ -50,7 +50,7 @@ class MoELayer:
         Wu = inp.Wu.to(self.device)
         Wd = inp.Wd.to(self.device)
         scales = None
-        if cfg.fp8_weights:
+        if cfg.quant_weights:
             scales = tuple(t.to(self.device) for t in (inp.Sg, inp.Su, inp.Sd))
         if paged:
             # prepacked experts in two pinned host planes, expert after expert,

@@ -11,7 +11,7 @@ from oracle import oracle as oracle_mod
 from routed_expert_ffn_top_amd import binding as B
 from routed_expert_ffn_top_amd.inputs import LayerInputs, MoEConfig, make_inputs
 
-TOL = {"bf16": 1e-2, "f32": 1e-5, "bf16_fp8w": 1e-2}
+TOL = {"bf16": 1e-2, "f32": 1e-5, "bf16_fp8w": 1e-2, "bf16_fp4w": 1e-2}
 ALPHA_TOL = 1e-6
 
 
@@ -49,13 +49,18 @@ class OracleRun:
 
     def weights(self):
         """Weights as the oracle takes them; fp8 codes are decoded by the
-        oracle itself and come with their row scales."""
+        oracle itself and come with their row scales; MXFP4 codes and block
+        scales are decoded by the oracle to plain weights."""
         if self._w is None:
             inp = self._inp
             if self.cfg.fp8_weights:
                 dec = lambda q: self.orc.fp8e4m3_decode(q.cpu().numpy())
                 self._w = (dec(inp.Wg), dec(inp.Wu), dec(inp.Wd))
                 self._scales = (np32(inp.Sg), np32(inp.Su), np32(inp.Sd))
+            elif self.cfg.fp4_weights:
+                dec = lambda q, s: self.orc.mxfp4_decode(q.cpu().numpy(), s.cpu().numpy())
+                self._w = (dec(inp.Wg, inp.Sg), dec(inp.Wu, inp.Su), dec(inp.Wd, inp.Sd))
+                self._scales = None
             else:
                 self._w = (np32(inp.Wg), np32(inp.Wu), np32(inp.Wd))
                 self._scales = None

@@ -246,6 +246,106 @@ def test_arena_fp8_strides_are_bytes_and_cover_the_scales():
     B.moe_arena_destroy(B.moe_arena_create(s, 0x100000, 0x40000000, gu, dn, 2))
 
 
+def _fp4_piece(rows):
+    return rows * 16 + (rows + 15) // 16 * 16
+
+
+def _fp4_unpack(o, N, K):
+    """Codes [N][K/2] and scales [N][K/32] of a packed MXFP4 slice, read back
+    from the layout stated for MOE_DT_BF16_FP4W; also checks the padding."""
+    codes = np.zeros((N, K // 2), np.uint8)
+    sc = np.zeros((N, K // 32), np.uint8)
+    off = 0
+    for b in range(0, N, 256):
+        rows = min(256, N - b)
+        for p in range(K // 32):
+            piece = o[off:off + _fp4_piece(rows)]
+            codes[b:b + rows, 16 * p:16 * p + 16] = piece[:rows * 16].reshape(rows, 16)
+            sc[b:b + rows, p] = piece[rows * 16:rows * 17]
+            assert not piece[rows * 17:].any(), "padding not zero"
+            off += _fp4_piece(rows)
+    assert off == o.size
+    return codes, sc
+
+
+def test_pack_gate_up_host_fp4_blocks():
+    """MXFP4: the packed gate/up slice holds the permuted rows' code bytes
+    and block scales piece by piece; 2f = 640 rows leave a 128-row block."""
+    f, d = 320, 128
+    s = B.make_shape(T=4, d=d, f=f, E=4, k=1, dtype="bf16_fp4w")
+    rng = np.random.default_rng(11)
+    cg, cu = (rng.integers(0, 256, size=(f, d // 2), dtype=np.uint8) for _ in range(2))
+    sg, su = (rng.integers(0, 256, size=(f, d // 32), dtype=np.uint8) for _ in range(2))
+    src_g = torch.from_numpy(np.concatenate([cg.reshape(-1), sg.reshape(-1)]))
+    src_u = torch.from_numpy(np.concatenate([cu.reshape(-1), su.reshape(-1)]))
+    n = B.fp4_slice_bytes(2 * f, d)
+    assert n == (d // 32) * (_fp4_piece(256) * 2 + _fp4_piece(128))
+    out = torch.full((n,), 0xAB, dtype=torch.uint8)
+    B.moe_pack_gate_up_host(s, src_g, src_u, out)
+    codes, sc = _fp4_unpack(out.numpy(), 2 * f, d)
+    for q in range(f // 32):
+        for w, (c, sv) in enumerate(((cg, sg), (cu, su))):
+            rr = slice(64 * q + 32 * w, 64 * q + 32 * w + 32)
+            assert np.array_equal(codes[rr], c[32 * q:32 * q + 32])
+            assert np.array_equal(sc[rr], sv[32 * q:32 * q + 32])
+
+
+def test_pack_down_host_fp4_blocks():
+    d, f = 320, 64    # a 64-row second block
+    s = B.make_shape(T=4, d=d, f=f, E=4, k=1, dtype="bf16_fp4w")
+    rng = np.random.default_rng(12)
+    c = rng.integers(0, 256, size=(d, f // 2), dtype=np.uint8)
+    sv = rng.integers(0, 256, size=(d, f // 32), dtype=np.uint8)
+    out = torch.full((B.fp4_slice_bytes(d, f),), 0xCD, dtype=torch.uint8)
+    B.moe_pack_down_host(s, torch.from_numpy(np.concatenate([c.reshape(-1), sv.reshape(-1)])), out)
+    codes, sc = _fp4_unpack(out.numpy(), d, f)
+    assert np.array_equal(codes, c) and np.array_equal(sc, sv)
+
+
+def test_arena_fp4_strides_are_bytes_of_the_packed_slices():
+    f, d = 256, 128
+    s = B.make_shape(T=16, d=d, f=f, E=8, k=2, P=4, dtype="bf16_fp4w")
+    gu, dn = B.fp4_slice_bytes(2 * f, d), B.fp4_slice_bytes(d, f)
+    with pytest.raises(B.MoEError):
+        B.moe_arena_create(s, 0x100000, 0x40000000, gu - 16, dn, 2)
+    with pytest.raises(B.MoEError):
+        B.moe_arena_create(s, 0x100000, 0x40000000, gu, dn - 16, 2)
+    B.moe_arena_destroy(B.moe_arena_create(s, 0x100000, 0x40000000, gu, dn, 2))
+
+
+def test_mxfp4_quantiser_round_trip():
+    """The seeded MXFP4 weights: decoded by the oracle, each weight is within
+    half an E2M1 step (times its block scale) of the fp32 draw, except where
+    it saturates at 6 times the scale; the scale byte is floor(log2 amax) - 2
+    + 127; values already on the grid come back unchanged."""
+    from oracle import oracle as oracle_mod
+    from routed_expert_ffn_top_amd.inputs import quantize_mxfp4
+    orc = oracle_mod.get()
+    gen = torch.Generator().manual_seed(3)
+    W = torch.randn((2, 8, 128), generator=gen) * 0.02
+    W[0, 0, :32] = 0.0                                   # an all-zero block
+    grid = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    W[1, 1, :32] = grid.repeat(4) * 2.0 ** -7 * torch.tensor([1.0, -1.0]).repeat(16)
+    codes, sc = quantize_mxfp4(W)
+    assert codes.shape == (2, 8, 64) and sc.shape == (2, 8, 4)
+    dec = orc.mxfp4_decode(codes.numpy(), sc.numpy()).astype(np.float64)
+    Wb = W.double().numpy().reshape(2, 8, 4, 32)
+    amax = np.abs(Wb).max(-1)
+    s = sc.numpy().astype(np.int64) - 127
+    nz = amax > 0
+    assert np.array_equal(s[nz], np.floor(np.log2(amax[nz])).astype(np.int64) - 2)
+    assert (s[~nz] == -127).all()
+    scale = np.ldexp(1.0, s)[..., None]
+    err = np.abs(dec.reshape(2, 8, 4, 32) - Wb)
+    sat = np.abs(Wb) > 6 * scale
+    # step between neighbouring E2M1 values: 0.5 below 2, 1 in [2, 4), 2 above
+    step = np.where(np.abs(Wb) < 2 * scale, 0.5, np.where(np.abs(Wb) < 4 * scale, 1.0, 2.0)) * scale
+    assert (err[~sat] <= step[~sat] / 2 + 1e-12).all()
+    assert np.allclose(np.abs(dec.reshape(2, 8, 4, 32))[sat], (6 * scale * np.ones_like(Wb))[sat])
+    assert np.array_equal(dec[1, 1, :32], W[1, 1, :32].double().numpy())
+    assert not dec[0, 0, :32].any()
+
+
 class _FakeArena:
     def __init__(self, handle):
         self.handle = handle

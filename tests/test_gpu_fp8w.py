@@ -113,14 +113,14 @@ def test_fp8w_edge_shapes():
         _check_layer(MID8.with_(T=T, name=f"mid_fp8w_T{T}"))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "bf16_fp8w"])
+@pytest.mark.parametrize("dtype", ["bf16", "bf16_fp8w", "bf16_fp4w"])
 def test_device_pack_equals_host_pack(dtype):
     say(f"gate/up and down packing on the device equal the host packing ({dtype})")
     cfg = MID.with_(dtype=dtype, E=3, k=2, T=4)
     inp = gpu_inputs(cfg)
     s = B.make_shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, P=cfg.E, dtype=dtype)
     arena = B.Arena(s)
-    scales = (inp.Sg, inp.Su, inp.Sd) if cfg.fp8_weights else None
+    scales = (inp.Sg, inp.Su, inp.Sd) if cfg.quant_weights else None
     for e in range(cfg.E):
         g, u, dn = B.expert_slices(inp.Wg, inp.Wu, inp.Wd, scales, e)
         dev = torch.empty_like(arena.plane_gu[0])
