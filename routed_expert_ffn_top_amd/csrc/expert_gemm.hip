@@ -449,7 +449,10 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     f32x16_t acc[MI][NI];
     bf16x8_t af[2][MI], bfr[2][NI];
     u32x2_t braw[2][NI];   // fp8 weights: 8 codes per fragment, converted in mfmas
-    uint32_t b4raw[2][NI], b4sc[2][NI];   // MXFP4: 8 codes and the row's scale byte per fragment
+    // MXFP4: 8 codes per fragment; the row's block scale (one per stage, so
+    // read with the step-0 fragments and carried over to step 1)
+    uint32_t b4raw[2][NI];
+    float b4sc[2][NI];
     const int c4[2] = {(0 + (lane >> 5)) * 4, (2 + (lane >> 5)) * 4};   // code bytes of chunk 2*ks + (lane >> 5)
     // fp8 fragment of B row (lane & 31): 8-byte piece c = 2*ks + (lane >> 5) of
     // the 32-byte row, stored in 16-byte half (c >> 1) ^ ((row >> 3) & 1)
@@ -470,7 +473,10 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 b4raw[set][j] = *(const uint32_t *)(Bs + (r0 + j * 32) * 16 + c4[ks]);
-                b4sc[set][j] = *(const uint8_t *)(Bs + BN * 16 + r0 + j * 32);
+                if (ks == 0)
+                    b4sc[set][j] = e8m0_to_f32(*(const uint8_t *)(Bs + BN * 16 + r0 + j * 32));
+                else   // step 1 of the stage whose step-0 fragments are in set 0
+                    b4sc[set][j] = b4sc[0][j];
             }
         } else {
             const char *Bs = lds + stage * STAGE + BM * ROWB + wn * TN * ROWB + foff[ks];
@@ -485,7 +491,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
         }
         if constexpr (BF4) {
 #pragma unroll
-            for (int j = 0; j < NI; ++j) bfr[set][j] = fp4x8_to_bf16(b4raw[set][j], e8m0_to_f32(b4sc[set][j]));
+            for (int j = 0; j < NI; ++j) bfr[set][j] = fp4x8_to_bf16(b4raw[set][j], b4sc[set][j]);
         }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -495,7 +501,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
     };
     // interleave: the (MI + NI) fragment reads of the next step are spread
     // over the MI * NI MFMAs of this step
-    constexpr int NRD = MI + (BF4 ? 2 : 1) * NI;   // LDS reads per step (BF4: codes and scale)
+    constexpr int NRD = MI + NI;   // LDS reads per step (BF4: the scale reads of step 0 ride along)
     auto interleave = [&]() {
 #pragma unroll
         for (int q = 0; q < (NRD < MI * NI ? NRD : MI * NI); ++q) {
