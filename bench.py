@@ -120,7 +120,7 @@ def summarize_pmc(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, out, c
         if not hits:
             raise SystemExit(f"no matching kernel in {list(d)[:5]}")
         return max(hits.items(), key=lambda kv: kv[1][0])
-    is_gu = lambda k: "k_gemm_mfma_lds<" in k and ", true, false>" in k   # gate/up, bf16 weights
+    is_gu = lambda k: "k_gemm_mfma_lds<" in k and ", true, false, false>" in k   # gate/up, bf16 weights
     is_copy = lambda k: "elementwise" in k.lower() and "Mul" in k
     gf_name, (gf, gfn) = pick(_pmc_per_kernel(fetch_csv, "FETCH_SIZE"), is_gu)
     gw_name, (gw, gwn) = pick(_pmc_per_kernel(write_csv, "WRITE_SIZE"), is_gu)
@@ -159,8 +159,8 @@ LAYER_KERNELS = (
     ("top-k", lambda k: "k_topk<" in k),
     ("route count", lambda k: "k_route_count" in k),
     ("route place", lambda k: "k_route_place" in k),
-    ("gate/up", lambda k: "k_gemm_mfma_lds<" in k and ", true, false>" in k),
-    ("down", lambda k: "k_gemm_mfma_lds<" in k and ", false, false>" in k),
+    ("gate/up", lambda k: "k_gemm_mfma_lds<" in k and ", true, false, false>" in k),
+    ("down", lambda k: "k_gemm_mfma_lds<" in k and ", false, false, false>" in k),
     ("combine", lambda k: "k_combine<" in k),
 )
 
