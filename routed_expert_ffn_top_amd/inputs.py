@@ -197,17 +197,15 @@ def quantize_mxfp4(W: torch.Tensor):
     s = torch.where(amax > 0, e.to(torch.int32) - 1 - 2, torch.full_like(e, -127, dtype=torch.int32))
     s = s.clamp(-127, 127)
     v = (Wb / torch.ldexp(torch.ones_like(amax), s.to(torch.float32)).unsqueeze(-1)).abs()
-    # nearest E2M1 magnitude, ties to the even code (midpoints between
-    # neighbouring values go to the one whose code is even)
-    grid = torch.tensor(E2M1_VALUES, dtype=torch.float32, device=W.device)
-    dist = (v.unsqueeze(-1) - grid).abs()
-    best = dist.min(dim=-1, keepdim=True).values
-    cand = (dist == best)
-    codes_idx = torch.arange(8, device=W.device)
-    # among tied candidates prefer the even code
-    pref = torch.where(cand, (codes_idx % 2) * 16 + codes_idx, torch.full_like(codes_idx, 99))
-    mag = pref.min(dim=-1).values % 16
-    mag = torch.where(v >= 6.0, torch.full_like(mag, 7), mag)
+    # nearest E2M1 magnitude: bucketize against the midpoints between
+    # neighbouring values (a value on a midpoint lands on the lower one), then
+    # move midpoint ties from an odd code to the even code above; beyond 6
+    # saturates at code 7
+    mids = torch.tensor([(a + b) / 2 for a, b in zip(E2M1_VALUES, E2M1_VALUES[1:])],
+                        dtype=torch.float32, device=W.device)
+    mag = torch.bucketize(v, mids)
+    tie = (mag < 7) & (v == mids[mag.clamp(max=6)])
+    mag = torch.where(tie & (mag % 2 == 1), mag + 1, mag)
     sign = (Wb < 0) & (mag > 0)
     code = (mag + 8 * sign.to(mag.dtype)).to(torch.uint8).reshape(*lead, rows, K)
     packed = code[..., 0::2] | (code[..., 1::2] << 4)
