@@ -316,7 +316,10 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X,
  * src_stride and destination stride dst_stride (elements; bytes for
  * MOE_DT_BF16_FP8W, whose source slices are row-major codes followed by one
  * fp32 scale per row, and whose packed slices keep their row scales after
- * the codes, in the packed row order and untiled).
+ * the codes, in the packed row order and untiled; bytes for MOE_DT_BF16_FP4W,
+ * whose slices are described with that dtype). Sources, destination and
+ * strides must be 4-byte aligned (the kernels move 32-bit words); otherwise
+ * MOE_ERR_INVALID_ARG.
  * moe_pack_gate_up_host / moe_pack_down_host: the same on host memory, one
  * expert, synchronous.
  */

@@ -549,6 +549,8 @@ moe_status moe_pack_gate_up(const moe_shape *shape, const void *W_g, const void 
         return fail(MOE_ERR_INVALID_ARG, "pack: strides smaller than a slice");
     if (((src_stride * esz) % 4) != 0 || ((dst_stride * esz) % 4) != 0)
         return fail(MOE_ERR_INVALID_ARG, "pack: strides must be whole 32-bit words");
+    if (!aligned(W_g, 4) || !aligned(W_u, 4) || !aligned(dst, 4))
+        return fail(MOE_ERR_INVALID_ARG, "pack: sources and destination must be 4-byte aligned");
     HIP_TRY(launch_pack_gate_up(*shape, W_g, W_u, dst, n, src_stride, dst_stride, S(stream)), "pack launch");
     return MOE_OK;
 }
@@ -609,6 +611,8 @@ moe_status moe_pack_down(const moe_shape *shape, const void *W_d, void *dst, int
         return fail(MOE_ERR_INVALID_ARG, "pack: strides smaller than a slice");
     if (((src_stride * esz) % 4) != 0 || ((dst_stride * esz) % 4) != 0)
         return fail(MOE_ERR_INVALID_ARG, "pack: strides must be whole 32-bit words");
+    if (!aligned(W_d, 4) || !aligned(dst, 4))
+        return fail(MOE_ERR_INVALID_ARG, "pack: sources and destination must be 4-byte aligned");
     HIP_TRY(launch_pack_down(*shape, W_d, dst, n, src_stride, dst_stride, S(stream)), "pack launch");
     return MOE_OK;
 }

@@ -386,3 +386,18 @@ def test_arena_table_on_host():
         assert ei.value.status == B.MOE_ERR_INVALID_ARG
     finally:
         B.moe_arena_destroy(h)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "bf16_fp8w", "bf16_fp4w"])
+def test_device_pack_rejects_misaligned_pointers(dtype):
+    """The packing kernels move 32-bit words: a source or destination that is
+    not 4-byte aligned is refused before anything is launched."""
+    s = B.make_shape(T=4, d=128, f=128, E=4, k=1, dtype=dtype)
+    for g, u, dst in ((0x100002, 0x200000, 0x300000), (0x100000, 0x200001, 0x300000),
+                      (0x100000, 0x200000, 0x300003)):
+        with pytest.raises(B.MoEError) as ei:
+            B.moe_pack_gate_up(s, g, u, dst, 1, 0, 0, stream=0)
+        assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoEError) as ei:
+        B.moe_pack_down(s, 0x100002, 0x300000, 1, 0, 0, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
