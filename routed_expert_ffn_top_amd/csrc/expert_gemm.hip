@@ -858,6 +858,11 @@ hipError_t launch_simple(const GemmArgs &a, int max_rows, hipStream_t st)
 #ifndef MOE_DOWN_TILE
 #define MOE_DOWN_TILE MOE_RING_TILE
 #endif
+// MXFP4 weights: 2 wave rows x 4 wave columns, so that each weight fragment
+// is decoded by 2 waves instead of 4 (bf16 and fp8 measured slower so).
+#ifndef MOE_FP4_TILE
+#define MOE_FP4_TILE 256, 256, 4, 2, 4
+#endif
 
 hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
                           hipStream_t st)
@@ -868,6 +873,7 @@ hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, b
         if (a.bfp8 || a.bfp4) return hipErrorInvalidValue;   // the plain kernel reads bf16 weights only
         return launch_simple<uint16_t, true>(a, max_rows, st);
     }
+    if (a.bfp4) return launch_mfma_lds<MOE_FP4_TILE, true>(a, max_rows, st);
     return launch_mfma_lds<MOE_RING_TILE, true>(a, max_rows, st);
 }
 
@@ -880,6 +886,7 @@ hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool
         if (a.bfp8 || a.bfp4) return hipErrorInvalidValue;
         return launch_simple<uint16_t, false>(a, max_rows, st);
     }
+    if (a.bfp4) return launch_mfma_lds<MOE_FP4_TILE, false>(a, max_rows, st);
     return launch_mfma_lds<MOE_DOWN_TILE, false>(a, max_rows, st);
 }
 
