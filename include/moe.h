@@ -26,7 +26,9 @@
  *    are left out, and moe_device_errors() reports and clears the word.
  *  - Index tensors are int32, route weights and logits fp32, the output
  *    accumulator fp32. X, the expert weights and the intermediate H use
- *    moe_shape.dtype (bf16 or fp32).
+ *    moe_shape.dtype (bf16 or fp32); with MOE_DT_BF16_FP8W and
+ *    MOE_DT_BF16_FP4W, X and H are bf16 and the expert weights are stored
+ *    quantised (formats below).
  *  - Route numbering: route i = t * K' + j sends token t to its rank-j
  *    expert, K' = k + n_shared. Ranks 0..k-1 are the routed top-k in
  *    descending logit order; ranks k..K'-1 are the shared experts
@@ -125,7 +127,7 @@ typedef struct moe_shape {
     int32_t n_shared;
     int32_t P;
     int32_t capacity; /* C, >= 1 */
-    int32_t dtype;    /* MOE_DT_BF16, MOE_DT_BF16_FP8W or MOE_DT_F32 */
+    int32_t dtype;    /* MOE_DT_BF16, MOE_DT_BF16_FP8W, MOE_DT_BF16_FP4W or MOE_DT_F32 */
     int32_t renorm;   /* 1: top-k weights renormalised over the k selected */
     int64_t ldx;      /* row stride of X in elements, >= d */
     int64_t ldy;      /* row stride of Y in elements, >= d, multiple of 4 */
