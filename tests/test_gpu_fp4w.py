@@ -107,3 +107,31 @@ def test_fp4w_quantisation_error_is_bounded():
     d = rel_err(f4, fb.astype(np.float64))
     say(f"  rel diff MXFP4 vs bf16 weights: {d:.3e}")
     assert d < 0.5
+
+
+def _random_scales(inp, seed):
+    """Replace the quantiser's block scales (nearly all the same byte for these
+    draws) by seeded bytes in [112, 128], about 2 % of them 0 (2^-127), so
+    that a scale taken from the wrong row or K block changes the result."""
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    for name in ("Sg", "Su", "Sd"):
+        S = getattr(inp, name)
+        R = torch.randint(112, 129, S.shape, generator=gen, device="cuda", dtype=torch.int32)
+        Z = torch.rand(S.shape, generator=gen, device="cuda") < 0.02
+        setattr(inp, name, torch.where(Z, torch.zeros_like(R), R).to(torch.uint8).contiguous())
+    return inp
+
+
+@pytest.mark.parametrize("cfg", [MID4, MoEConfig(name="ragged_fp4w_scales", index=34, T=120, d=320, f=192, E=6,
+                                                   k=2, dtype="bf16_fp4w")], ids=["mid", "ragged"])
+def test_fp4w_random_block_scales(cfg):
+    say(f"MXFP4 weights with random block scales ({cfg.name})")
+    inp = _random_scales(gpu_inputs(cfg), seed=5 + cfg.index)
+    assert len(torch.unique(inp.Sd)) > 10
+    layer = MoELayer(inp)
+    Y = inp.A.clone()
+    layer.forward(Y)
+    torch.cuda.synchronize()
+    err = rel_err(np32(Y), OracleRun(inp).Y())
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL[cfg.dtype], err
