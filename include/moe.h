@@ -97,7 +97,8 @@ typedef void *moe_stream; /* a hipStream_t */
 #define MOE_FFN_SIMPLE_KERNEL 4 /* bf16: run the projections with the plain
                                    LDS-tiled vector-ALU kernel instead of the
                                    MFMA kernel (an independent second path);
-                                   MOE_ERR_UNSUPPORTED with fp8 weights */
+                                   MOE_ERR_UNSUPPORTED with fp8 or MXFP4
+                                   weights */
 
 /* Residency states (section 3.3, "Bounded Parameter Arena and Safe Slot Reuse") */
 #define MOE_SLOT_AVAILABLE 0
