@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import OracleRun, TOL, check_y, gpu_inputs, np32, rel_err, sample_tokens, say
+from gpu_util import OracleRun, TOL, check_y, gpu_inputs, np32, rel_err, say
 from routed_expert_ffn_top_amd import binding as B
 from routed_expert_ffn_top_amd.inputs import CONFIGS, MoEConfig
 from routed_expert_ffn_top_amd.layer import MoELayer
@@ -38,16 +38,16 @@ def test_layer_ragged_weight_blocks_fp4w():
     _check_layer(MoEConfig(name="ragged_fp4w", index=33, T=150, d=320, f=128, E=8, k=2, dtype="bf16_fp4w"))
 
 
-def test_layer_olmoe_t4096_fp4w_sampled():
-    say("layer OLMoE T=4096, MXFP4 weights (sampled rows)")
+def test_layer_olmoe_t4096_fp4w():
+    say("layer OLMoE T=4096, MXFP4 weights, every token")
     cfg = CONFIGS["olmoe_t4096_fp4w"]
-    _check_layer(cfg, tokens=sample_tokens(cfg.T, 96))
+    _check_layer(cfg)
 
 
-def test_layer_mixtral_t256_fp4w_sampled():
-    say("layer Mixtral T=256, MXFP4 weights, split-K down (sampled rows)")
+def test_layer_mixtral_t256_fp4w():
+    say("layer Mixtral T=256, MXFP4 weights, split-K down, every token")
     cfg = CONFIGS["mixtral_t256_fp4w"]
-    _check_layer(cfg, tokens=sample_tokens(cfg.T, 24))
+    _check_layer(cfg)
 
 
 def test_fp4w_edge_shapes():
@@ -94,7 +94,7 @@ def test_paged_equals_resident_fp4w():
         torch.cuda.synchronize()
         assert torch.equal(Y, y_res), "paging changed the output"
     orun = OracleRun(inp)
-    toks = sample_tokens(cfg.T, 48)
+    toks = np.arange(cfg.T)
     check_y(np32(Y)[toks], orun.Y(tokens=toks), np32(inp.A)[toks], cfg.dtype)
 
 

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import OracleRun, TOL, check_y, gpu_inputs, np32, rel_err, sample_tokens, say
+from gpu_util import OracleRun, TOL, check_y, gpu_inputs, np32, rel_err, say
 from routed_expert_ffn_top_amd import binding as B
 from routed_expert_ffn_top_amd.inputs import CONFIGS
 from routed_expert_ffn_top_amd.layer import MoELayer
@@ -32,16 +32,16 @@ def test_layer_shared_experts_fp8w():
     _check_layer(MID8_SHARED)
 
 
-def test_layer_olmoe_t4096_fp8w_sampled():
-    say("layer OLMoE T=4096, fp8 weights (sampled rows)")
+def test_layer_olmoe_t4096_fp8w():
+    say("layer OLMoE T=4096, fp8 weights, every token")
     cfg = CONFIGS["olmoe_t4096_fp8w"]
-    _check_layer(cfg, tokens=sample_tokens(cfg.T, 96))
+    _check_layer(cfg)
 
 
-def test_layer_mixtral_t256_fp8w_sampled():
-    say("layer Mixtral T=256, fp8 weights, split-K down (sampled rows)")
+def test_layer_mixtral_t256_fp8w():
+    say("layer Mixtral T=256, fp8 weights, split-K down, every token")
     cfg = CONFIGS["mixtral_t256_fp8w"]
-    _check_layer(cfg, tokens=sample_tokens(cfg.T, 24))
+    _check_layer(cfg)
 
 
 def test_fp8w_step_by_step_and_capacity_split():
@@ -92,7 +92,7 @@ def test_paged_equals_resident_fp8w():
         torch.cuda.synchronize()
         assert torch.equal(Y, y_res), "paging changed the output"
     orun = OracleRun(inp)
-    toks = sample_tokens(cfg.T, 48)
+    toks = np.arange(cfg.T)
     check_y(np32(Y)[toks], orun.Y(tokens=toks), np32(inp.A)[toks], cfg.dtype)
 
 

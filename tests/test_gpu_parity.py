@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from gpu_util import (OracleRun, TOL, check_descriptors, check_y, check_topk, gpu_inputs, np32, rel_err,
-                      sample_tokens, say)
+                      say)
 from oracle import oracle as oracle_mod
 from routed_expert_ffn_top_amd import binding as B
 from routed_expert_ffn_top_amd.inputs import CONFIGS, MoEConfig, make_inputs, make_logits, random_phi
@@ -243,22 +243,22 @@ def test_layer_olmoe_t1024():
     _check_layer(CONFIGS["olmoe_t1024"])
 
 
-def test_layer_dsv2lite_t4096_sampled():
-    say("layer DSV2-Lite T=4096 (sampled rows)")
+def test_layer_dsv2lite_t4096():
+    say("layer DSV2-Lite T=4096, every token")
     cfg = CONFIGS["dsv2lite_t4096"]
-    _check_layer(cfg, tokens=sample_tokens(cfg.T, 96))
+    _check_layer(cfg)
 
 
-def test_layer_olmoe_t4096_sampled():
-    say("layer OLMoE T=4096 (sampled rows)")
+def test_layer_olmoe_t4096():
+    say("layer OLMoE T=4096, every token")
     cfg = CONFIGS["olmoe_t4096"]
-    _check_layer(cfg, tokens=sample_tokens(cfg.T, 96))
+    _check_layer(cfg)
 
 
-def test_layer_mixtral_t256_sampled():
-    say("layer Mixtral T=256 (sampled rows)")
+def test_layer_mixtral_t256():
+    say("layer Mixtral T=256, every token")
     cfg = CONFIGS["mixtral_t256"]
-    _check_layer(cfg, tokens=sample_tokens(cfg.T, 24))
+    _check_layer(cfg)
 
 
 def test_deterministic_and_phi_independent():
@@ -318,7 +318,7 @@ def test_paged_equals_resident():
     counts = np.bincount(paged.routes["topk_idx"].cpu().numpy().reshape(-1), minlength=cfg.E)
     say(f"  experts with no routes: {int((counts == 0).sum())}")
     orun = OracleRun(inp)
-    toks = sample_tokens(cfg.T, 48)
+    toks = np.arange(cfg.T)
     check_y(np32(Y)[toks], orun.Y(tokens=toks), np32(inp.A)[toks], "bf16")
 
 
