@@ -255,6 +255,11 @@ def test_layer_olmoe_t4096():
     _check_layer(cfg)
 
 
+def test_layer_mixtral_t4096():
+    say("layer Mixtral T=4096 (4 row blocks per expert), every token")
+    _check_layer(CONFIGS["mixtral_t4096"], repeats=2)
+
+
 def test_layer_mixtral_t256():
     say("layer Mixtral T=256, every token")
     cfg = CONFIGS["mixtral_t256"]
