@@ -135,3 +135,37 @@ def test_device_pack_equals_host_pack(dtype):
         assert torch.equal(dev.cpu().view(torch.uint8), host.view(torch.uint8)), f"gate/up expert {e}"
         assert torch.equal(dev_d.cpu().view(torch.uint8), host_d.view(torch.uint8)), f"down expert {e}"
     arena.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "bf16_fp8w", "bf16_fp4w"])
+def test_device_pack_many_experts_strided(dtype):
+    say(f"packing 3 experts in one call, padded source strides ({dtype})")
+    cfg = MID.with_(dtype=dtype, E=3, k=2, T=4)
+    inp = gpu_inputs(cfg)
+    s = B.make_shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, P=cfg.E, dtype=dtype)
+    arena = B.Arena(s)
+    scales = (inp.Sg, inp.Su, inp.Sd) if cfg.quant_weights else None
+    sl = [B.expert_slices(inp.Wg, inp.Wu, inp.Wd, scales, e) for e in range(cfg.E)]
+    pad = 16 if cfg.quant_weights else 64     # keeps every source slice 4-byte aligned
+
+    def stack(parts):
+        n = parts[0].numel()
+        buf = torch.full((len(parts), n + pad), 7, dtype=parts[0].dtype, device="cuda")
+        for e, p in enumerate(parts):
+            buf[e, :n] = p.reshape(-1)
+        return buf, n + pad
+
+    g, sg = stack([x[0] for x in sl])
+    u, _ = stack([x[1] for x in sl])
+    dn, sd = stack([x[2] for x in sl])
+    B.moe_pack_gate_up(s, g, u, arena.plane_gu, cfg.E, sg, arena.stride_gu)
+    B.moe_pack_down(s, dn, arena.plane_d, cfg.E, sd, arena.stride_d)
+    torch.cuda.synchronize()
+    for e in range(cfg.E):
+        host = torch.empty_like(arena.plane_gu[e], device="cpu")
+        B.moe_pack_gate_up_host(s, sl[e][0].cpu(), sl[e][1].cpu(), host)
+        host_d = torch.empty_like(arena.plane_d[e], device="cpu")
+        B.moe_pack_down_host(s, sl[e][2].cpu(), host_d)
+        assert torch.equal(arena.plane_gu[e].cpu().view(torch.uint8), host.view(torch.uint8)), f"gate/up {e}"
+        assert torch.equal(arena.plane_d[e].cpu().view(torch.uint8), host_d.view(torch.uint8)), f"down {e}"
+    arena.close()
