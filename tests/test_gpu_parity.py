@@ -339,3 +339,25 @@ def test_edge_shapes():
     layer.forward(Y)
     torch.cuda.synchronize()
     assert Y.shape == (0, MID.d)
+
+
+@pytest.mark.parametrize("cfg,padx,pady", [(MID, 72, 36), (CONFIGS["tiny_fp32"], 12, 4)], ids=["bf16", "fp32"])
+def test_layer_row_strides(cfg, padx, pady):
+    """X and Y with row strides wider than d: the same bits as the contiguous
+    layer, and Y's padding columns untouched."""
+    say(f"layer with row strides ldx = d + {padx}, ldy = d + {pady} ({cfg.name})")
+    inp = gpu_inputs(cfg)
+    layer = MoELayer(inp)
+    y_ref = _layer_out(layer, inp)
+    d = cfg.d
+    s2 = B.make_shape(cfg.T, d, cfg.f, cfg.E, cfg.k, cfg.n_shared, P=layer.shape.P, dtype=cfg.dtype,
+                      renorm=cfg.renorm, ldx=d + padx, ldy=d + pady)
+    Xp = torch.full((cfg.T, d + padx), 1000.0, dtype=inp.X.dtype, device="cuda")   # read by mistake: wrong y
+    Xp[:, :d] = inp.X
+    Yp = torch.full((cfg.T, d + pady), 123.0, dtype=torch.float32, device="cuda")
+    Yp[:, :d] = inp.A
+    B.moe_layer_prefill(s2, Xp, layer.Wr, layer.bias, None, Yp, layer.arena, None, None,
+                        B.alloc_routes(s2), B.alloc_workspace(s2))
+    torch.cuda.synchronize()
+    assert torch.equal(Yp[:, :d], y_ref), "strided layer differs from the contiguous one"
+    assert bool((Yp[:, d:] == 123.0).all()), "padding columns of Y were written"
