@@ -361,3 +361,17 @@ def test_layer_row_strides(cfg, padx, pady):
     torch.cuda.synchronize()
     assert torch.equal(Yp[:, :d], y_ref), "strided layer differs from the contiguous one"
     assert bool((Yp[:, d:] == 123.0).all()), "padding columns of Y were written"
+
+
+def test_layer_with_given_logits():
+    """moe_layer_prefill with router logits passed in (no W_r): top-k ids,
+    route weights and output against the oracle on the same logits."""
+    say("layer with given logits")
+    inp = gpu_inputs(MID_SHARED)
+    layer = MoELayer(inp)
+    L = make_logits(MID_SHARED.T, MID_SHARED.E, seed=3, scale=2.0, device="cuda")
+    Y = _layer_out(layer, inp, logits=L)
+    orun = OracleRun(inp, logits=L.cpu().numpy())
+    check_topk(layer.routes, orun)
+    err, ffn = check_y(np32(Y), orun.Y(), np32(inp.A), MID_SHARED.dtype)
+    say(f"  rel err {err:.3e}, expert sum {ffn:.3e}")
