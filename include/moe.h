@@ -210,8 +210,12 @@ moe_status moe_device_errors(const moe_shape *shape, void *ws, size_t ws_bytes,
  * W_r[e] with each term one fused multiply-add, in this order: the hidden
  * index is cut into runs of 8 consecutive values, run r = i / 8 feeds partial
  * sum r % 16, each partial sum is a chain in ascending i starting from 0, and
- * s = ((p0 + p1) + p2) + ... + p15. This fixes the bits of every logit, so
- * the top-k decision is reproducible.
+ * s = ((p0 + p1) + p2) + ... + p15. The pages fix no evaluation order; this
+ * one fixes the bits of every logit, so the logits and the top-k decision
+ * taken on them are run-to-run reproducible. Each logit is within
+ * gamma_n * (sum_i |X[t][i] W_r[e][i]| + |bias[e]|) of the exact value,
+ * n = 8 * ceil(d / 128) + 16 roundings, gamma_n = n u / (1 - n u),
+ * u = 2^-24 (recursive summation with fused products).
  */
 moe_status moe_router_logits(const moe_shape *shape, const void *X,
                              const float *W_r, const float *bias,

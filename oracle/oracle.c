@@ -10,12 +10,10 @@
  *
  * Every function computes its result from the definition, with no blocking,
  * fusion or reordering:
- *   oracle_router_logits  L = X W_r (+ bias), fp32, one fused multiply-add
- *                         per term: 16 partial chains over interleaved runs
- *                         of 8 hidden indices, each in ascending index order,
- *                         then added in ascending chain order.  The top-k
- *                         decision is taken on these fp32 values, so this
- *                         order is part of the contract.
+ *   oracle_router_logits  L = X W_r (+ bias): the dot product and the bias
+ *                         summed in fp64 (every product of two fp32 values
+ *                         is exact there) and rounded once to fp32.  No
+ *                         evaluation order is part of the definition.
  *   oracle_topk           top-k of E experts per token (section 2.2: "a router
  *                         assigns each token to the top-k of E experts"), ties
  *                         to the lower expert id; softmax weights in fp64,
@@ -68,13 +66,16 @@ void oracle_set_threads(int n)
 }
 
 /*
- * Router logits. L[t][e] = sum over i = 0..d-1 of X[t][i] * Wr[i][e] in fp32,
- * evaluated in one fixed order. The hidden index is cut into runs of 8
- * consecutive values; run r = i / 8 feeds partial sum c = r mod 16. Each
- * partial sum is one fused multiply-add chain p[c] = fmaf(X[t][i], Wr[i][e],
- * p[c]) over its indices in ascending order, from p[c] = 0.0f. The 16 partial
- * sums are then added left to right, s = ((p[0] + p[1]) + p[2]) + ... + p[15],
- * and L = s + bias[e] (one fp32 addition) when a bias is given.
+ * Router logits (section 2.2: the router scores every expert for every
+ * token; the scores are the linear map X W_r, plus a per-expert bias when
+ * one is given). L[t][e] is the fp32 value nearest to
+ *   sum over i = 0..d-1 of X[t][i] * Wr[i][e]  (+ bias[e]),
+ * taken as: every product formed in fp64 (exact: two 24-bit significands
+ * fit in 53 bits), the products and the bias added in fp64 in ascending i,
+ * and the fp64 total rounded once to fp32 (round to nearest even).  The fp64
+ * sum differs from the exact one by at most (d + 1) 2^-53 sum |x w|, far
+ * below half an fp32 unit, so L is the correctly rounded logit except when
+ * the exact value lies that close to an fp32 rounding boundary.
  * X: [T][ldx] fp32 values (bf16 inputs widened exactly), Wr: [d][E], bias: [E]
  * or NULL, L: [T][E].
  */
@@ -86,16 +87,11 @@ void oracle_router_logits(int64_t T, int64_t d, int64_t E, const float *X,
 #pragma omp parallel for schedule(static)
     for (t = 0; t < T; ++t) {
         for (int64_t e = 0; e < E; ++e) {
-            float p[16];
-            for (int c = 0; c < 16; ++c) p[c] = 0.0f;
-            for (int64_t i = 0; i < d; ++i) {
-                const int c = (int)((i >> 3) & 15);
-                p[c] = fmaf(X[t * ldx + i], Wr[i * E + e], p[c]);
-            }
-            float s = p[0];
-            for (int c = 1; c < 16; ++c) s = s + p[c];
-            if (bias) s = s + bias[e];
-            L[t * E + e] = s;
+            double s = 0.0;
+            for (int64_t i = 0; i < d; ++i)
+                s += (double)X[t * ldx + i] * (double)Wr[i * E + e];
+            if (bias) s += (double)bias[e];
+            L[t * E + e] = (float)s;
         }
     }
 }

@@ -108,11 +108,133 @@ def check_descriptors(routes: dict, ref: dict, n_valid_expected=None):
 
 
 def check_topk(routes: dict, orun: OracleRun):
+    """Top-k ids and weights computed from the same logits on both sides
+    (logits passed in, not computed by the GPU router): ids bit-exact,
+    weights within ALPHA_TOL."""
     idx = routes["topk_idx"].cpu().numpy()
     assert np.array_equal(idx, orun.idx), "top-k ids differ"
     w = routes["topk_w"].cpu().numpy().astype(np.float64)
     rel = np.max(np.abs(w - orun.alpha) / np.maximum(np.abs(orun.alpha), 1e-30))
     assert rel <= ALPHA_TOL, f"alpha rel err {rel}"
+
+
+# ---------------------------------------------------------------------------
+# GPU router logits against the oracle's.
+#
+# The oracle's logit is the definition: the exact dot product plus the bias,
+# rounded once to fp32 (its fp64 sum adds at most (d + 1) 2^-53 sum|x w|).
+# The GPU router evaluates the same sum in fp32 in the fixed order its C ABI
+# documents: runs of 8 hidden indices, run r feeding partial sum r mod 16,
+# each partial sum a chain of m = 8 ceil(d / 128) fused multiply-adds, then 15
+# additions of the partial sums and one of the bias. Each of those n = m + 16
+# steps rounds once, so (Higham, recursive summation)
+#   |L_gpu - exact| <= gamma_n (sum|x w| + |b|),  gamma_n = n u / (1 - n u),
+# and |L_gpu - L_oracle| is bounded by that plus the oracle's own rounding.
+U32 = 2.0 ** -24
+
+
+def router_bound(X: np.ndarray, Wr: np.ndarray, bias, L_ref: np.ndarray) -> np.ndarray:
+    """Per-logit bound on |L_gpu - L_oracle|. X [T][d], Wr [d][E] (fp32 values)."""
+    d = X.shape[1]
+    n = 8 * ((d + 127) // 128) + 16
+    gamma = n * U32 / (1 - n * U32)
+    absdot = np.abs(X.astype(np.float64)) @ np.abs(Wr.astype(np.float64))
+    if bias is not None:
+        absdot = absdot + np.abs(bias.astype(np.float64))[None, :]
+    return gamma * absdot + U32 * np.abs(L_ref.astype(np.float64)) + (d + 1) * 2.0 ** -53 * absdot + 2.0 ** -140
+
+
+def gpu_logits(layer) -> np.ndarray:
+    """The GPU router's logits for a layer's X and W_r (moe_router_logits:
+    the same kernel and arguments as the layer's own router step)."""
+    s = layer.shape
+    L = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    B.moe_router_logits(s, layer.X, layer.Wr, layer.bias, L)
+    torch.cuda.synchronize()
+    return L.cpu().numpy()
+
+
+def check_logits(L_gpu: np.ndarray, orun: OracleRun) -> np.ndarray:
+    """|L_gpu - L_oracle| within router_bound everywhere; returns the bound."""
+    bound = router_bound(orun.X, orun.Wr, orun.bias, orun.L)
+    diff = np.abs(L_gpu.astype(np.float64) - orun.L.astype(np.float64))
+    assert np.all(np.isfinite(L_gpu)), "non-finite GPU logit"
+    assert np.all(diff <= bound), f"logit outside its bound: max diff/bound {np.max(diff / bound):.3g}"
+    return bound
+
+
+def _decided(L: np.ndarray, bound: np.ndarray, k: int) -> np.ndarray:
+    """Tokens whose oracle top-k (ids and their order) no logit error within
+    the bound can change: each of the first k + 1 values in descending order
+    exceeds the next by more than the two values' bounds."""
+    T, E = L.shape
+    Lk = np.where(np.isnan(L), -np.inf, L).astype(np.float64)
+    order = np.lexsort((np.tile(np.arange(E), (T, 1)), -Lk), axis=1)[:, :min(k + 1, E)]
+    v = np.take_along_axis(Lk, order, 1)
+    b = np.take_along_axis(bound, order, 1)
+    gaps = v[:, :-1] - v[:, 1:]
+    if gaps.shape[1] == 0:
+        return np.ones(T, dtype=bool)
+    return np.all(gaps > b[:, :-1] + b[:, 1:], axis=1)
+
+
+def check_routing_from_gpu_logits(routes: dict, orun: OracleRun, L_gpu: np.ndarray) -> np.ndarray:
+    """Top-k of a layer whose router ran on the GPU, against the oracle's
+    top-k on the oracle's logits.
+      - the GPU logits lie within router_bound of the oracle's;
+      - decided tokens (_decided) have bit-exact ids;
+      - every other token (a near tie) has a valid choice: each GPU pick e_j
+        could be the largest of the experts not yet picked under some logit
+        errors within the bound, L[e_j] + b[e_j] >= L[e] - b[e];
+      - route weights, where the ids agree, within ALPHA_TOL plus what the
+        measured logit difference moves a softmax weight: |d ln alpha| <=
+        2 max_e |L_gpu - L_oracle| over the token's logits.
+    Returns a mask of the tokens whose ids agree with the oracle's."""
+    cfg = orun.cfg
+    k = cfg.k
+    bound = check_logits(L_gpu, orun)
+    idx = routes["topk_idx"].cpu().numpy()
+    decided = _decided(orun.L, bound, k)
+    same = np.all(idx == orun.idx, axis=1)
+    assert np.all(same[decided]), f"{int((~same[decided]).sum())} decided tokens pick other experts"
+    Lk = np.where(np.isnan(orun.L), -np.inf, orun.L).astype(np.float64)
+    for t in np.nonzero(~decided)[0]:
+        left = np.ones(cfg.E, dtype=bool)
+        for j in range(k):
+            e = idx[t, j]
+            assert 0 <= e < cfg.E and left[e], f"token {t}: invalid pick {e}"
+            left[e] = False
+            if left.any():
+                assert Lk[t, e] + bound[t, e] >= np.max(Lk[t, left] - bound[t, left]), f"token {t} rank {j}"
+        assert np.array_equal(idx[t, k:], orun.idx[t, k:]), f"token {t}: shared ranks"
+    delta = np.max(np.abs(L_gpu.astype(np.float64) - orun.L.astype(np.float64)), axis=1)
+    w = routes["topk_w"].cpu().numpy().astype(np.float64)
+    rel = np.abs(w - orun.alpha) / np.maximum(np.abs(orun.alpha), 1e-30)
+    tol = ALPHA_TOL + 2.0001 * delta[:, None]
+    assert np.all(rel[same] <= tol[same]), f"alpha outside tolerance: max rel {np.max(rel[same]):.3g}"
+    say(f"  routing: {int((~decided).sum())} near-tie tokens of {len(idx)}, {int((~same).sum())} with "
+        f"other picks; max|dL| {np.max(delta):.3g}, max|dL|/bound {np.max(np.abs(L_gpu - orun.L) / bound):.3g}")
+    return same
+
+
+def check_layer_output(layer, inp: LayerInputs, Y: torch.Tensor, tokens=None, orun=None,
+                       descriptors=True):
+    """A layer run whose router ran on the GPU, against the oracle: routing by
+    check_routing_from_gpu_logits, the route map bit-exact (when the build
+    covered every route and no token picked other experts), and the output on
+    the requested tokens whose picks agree with the oracle's (every token, at
+    these seeds) within the dtype's tolerance. Returns (rel err, expert-sum
+    rel err, oracle run)."""
+    cfg = inp.cfg
+    orun = OracleRun(inp) if orun is None else orun
+    same = check_routing_from_gpu_logits(layer.routes, orun, gpu_logits(layer))
+    if descriptors and same.all() and layer.shape.capacity >= cfg.T * cfg.kp and not layer.paged:
+        ref = orun.route_map(layer.phi, layer.shape.P)
+        check_descriptors(layer.routes, ref, n_valid_expected=cfg.T * cfg.kp)
+    toks = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
+    toks = toks[same[toks]]
+    err, ffn = check_y(np32(Y)[toks], orun.Y(tokens=toks), np32(inp.A)[toks], cfg.dtype)
+    return err, ffn, orun
 
 
 def sample_tokens(T: int, n: int, seed: int = 7) -> np.ndarray:

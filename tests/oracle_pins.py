@@ -4,8 +4,9 @@ Each ``check_*`` takes an ``Oracle`` (any build of oracle.c) and raises
 AssertionError when the oracle disagrees with:
 
 * hand-worked closed forms (tests/golden/*.json);
-* exact integer arithmetic (router on inputs whose fp32 sums are exact);
-* the fp64 error bound of recursive summation;
+* exact integer arithmetic (router on inputs whose sums are exact);
+* exact rational arithmetic (router logits are the correctly rounded sums)
+  and math.fsum at the OLMoE hidden size;
 * a numpy/scipy brute force of a *different* formulation: top-k by lexsort,
   softmax by scipy, the route map by a stable argsort and bincount, and the
   layer as a dense masked sum over every expert on every token;
@@ -90,17 +91,18 @@ def _rel(a, b):
 
 # ---------------------------------------------------------------- router --
 def check_router_golden(orc):
-    for case in _load("router_chain.json")["cases"]:
-        x = np.array([case["x"]], dtype=np.float32)
-        w = np.array(case["w"], dtype=np.float32)[:, None]
-        b = np.array([case["bias"]], dtype=np.float32)
+    for case in _load("router_dot.json")["cases"]:
+        hx = lambda v: float.fromhex(v)
+        x = np.array([[hx(v) for v in case["x"]]], dtype=np.float32)
+        w = np.array([hx(v) for v in case["w"]], dtype=np.float32)[:, None]
+        b = np.array([hx(case["bias"])], dtype=np.float32)
         L = orc.router_logits(x, w, b)
-        assert L[0, 0] == np.float32(case["expect"]), (case["why"], L[0, 0])
+        assert L[0, 0] == np.float32(hx(case["expect"])), (case["why"], float(L[0, 0]).hex())
 
 
 def check_router_exact_integers(orc):
-    """Small integers scaled by 2^-4: every fp32 partial sum is exact, so
-    the logits equal the exact integer matrix product."""
+    """Small integers scaled by 2^-4: every partial sum is exact, so the
+    logits equal the exact integer matrix product."""
     rng = _rng(11)
     T, d, E = 17, 64, 8
     Xi = rng.integers(-8, 9, size=(T, d))
@@ -116,22 +118,58 @@ def check_router_exact_integers(orc):
     assert np.array_equal(L0.astype(np.float64), (Xi @ Wi) / 16.0)
 
 
-def check_router_error_bound(orc):
-    """|L - exact| <= gamma_n * sum|x w| with n = m + 15: each of the 16
-    partial chains holds at most m = 8 * ceil(d / 128) terms and the partial
-    sums take 15 more additions (Higham's bound for recursive summation, with
-    fused products rounded once)."""
+def _round_f32(q):
+    """The fp32 value nearest to the exact rational q, ties to the even
+    significand (q within the finite fp32 range)."""
+    from fractions import Fraction
+    f = np.float32(float(q))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda c: (abs(Fraction(float(c)) - q), int(np.array(c).view(np.uint32)) & 1))
+
+
+def check_router_correct_rounding(orc):
+    """Logits against exact rational arithmetic: every logit is the fp32
+    value nearest to the exact sum of the products and the bias (ties to
+    even), except where the exact value lies within the fp64 summation error
+    (d + 1) 2^-53 sum|x w| of an fp32 rounding boundary (none at these seeds)."""
+    from fractions import Fraction
     rng = _rng(12)
-    u = 2.0 ** -24
-    for T, d, E in ((9, 2048, 64), (5, 320, 8)):
+    T, d, E = 6, 96, 8
+    X = _bf16_values(rng.standard_normal((T, d), dtype=np.float32))
+    Wr = rng.standard_normal((d, E), dtype=np.float32) * np.float32(0.02)
+    b = rng.standard_normal(E, dtype=np.float32) * np.float32(0.5)
+    L = orc.router_logits(X, Wr, b)
+    near = 0
+    for t in range(T):
+        for e in range(E):
+            q = sum(Fraction(float(X[t, i])) * Fraction(float(Wr[i, e])) for i in range(d)) + Fraction(float(b[e]))
+            r = _round_f32(q)
+            if L[t, e] != r:
+                slack = (d + 1) * 2.0 ** -53 * float(np.abs(X[t].astype(np.float64)) @ np.abs(Wr[:, e].astype(np.float64)))
+                mid = (Fraction(float(L[t, e])) + Fraction(float(r))) / 2
+                assert abs(q - mid) <= Fraction(slack), (t, e, float(L[t, e]), float(r))
+                near += 1
+    assert near == 0
+
+
+def check_router_error_bound(orc):
+    """At the OLMoE hidden size: |L - s| <= half an fp32 unit of s plus
+    (d + 1) 2^-53 sum|x w|, where s is math.fsum of the exact fp64 products
+    and the bias (the correctly rounded fp64 sum)."""
+    import math
+    rng = _rng(13)
+    for T, d, E in ((4, 2048, 64), (5, 320, 8)):
         X = _bf16_values(rng.standard_normal((T, d), dtype=np.float32))
         Wr = rng.standard_normal((d, E), dtype=np.float32) * np.float32(0.02)
-        L = orc.router_logits(X, Wr, None).astype(np.float64)
-        exact = X.astype(np.float64) @ Wr.astype(np.float64)
-        n = 8 * ((d + 127) // 128) + 15
-        gamma = n * u / (1 - n * u)
-        bound = gamma * (np.abs(X.astype(np.float64)) @ np.abs(Wr.astype(np.float64)))
-        assert np.all(np.abs(L - exact) <= bound)
+        b = rng.standard_normal(E, dtype=np.float32) * np.float32(0.1)
+        L = orc.router_logits(X, Wr, b).astype(np.float64)
+        Xd, Wd = X.astype(np.float64), Wr.astype(np.float64)
+        for t in range(T):
+            for e in range(E):
+                s = math.fsum(list(Xd[t] * Wd[:, e]) + [float(b[e])])
+                half_ulp = float(np.spacing(np.float32(abs(s)))) / 2
+                slack = (d + 1) * 2.0 ** -53 * float(np.abs(Xd[t]) @ np.abs(Wd[:, e]))
+                assert abs(L[t, e] - s) <= half_ulp + slack, (t, e, L[t, e], s)
 
 
 # ----------------------------------------------------------------- top-k --
@@ -465,7 +503,8 @@ def check_layer_chain(orc):
     assert out["n_valid"] == T * k
 
 
-ALL_CHECKS = [check_router_golden, check_router_exact_integers, check_router_error_bound,
+ALL_CHECKS = [check_router_golden, check_router_exact_integers, check_router_correct_rounding,
+              check_router_error_bound,
               check_topk_bruteforce, check_topk_special, check_topk_nan_and_signed_zero, check_alpha,
               check_shared,
               check_route_map_golden, check_route_map_bruteforce, check_route_map_errors,

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import OracleRun, TOL, check_y, gpu_inputs, np32, rel_err, say
+from gpu_util import OracleRun, TOL, check_layer_output, check_y, gpu_inputs, np32, rel_err, say
 from routed_expert_ffn_top_amd import binding as B
 from routed_expert_ffn_top_amd.inputs import CONFIGS, MoEConfig
 from routed_expert_ffn_top_amd.layer import MoELayer
@@ -93,9 +93,7 @@ def test_paged_equals_resident_fp4w():
         paged.forward(Y, copy=copy)
         torch.cuda.synchronize()
         assert torch.equal(Y, y_res), "paging changed the output"
-    orun = OracleRun(inp)
-    toks = np.arange(cfg.T)
-    check_y(np32(Y)[toks], orun.Y(tokens=toks), np32(inp.A)[toks], cfg.dtype)
+    check_layer_output(paged, inp, Y)
 
 
 def test_fp4w_quantisation_error_is_bounded():
@@ -132,5 +130,5 @@ def test_fp4w_random_block_scales(cfg):
     Y = inp.A.clone()
     layer.forward(Y)
     torch.cuda.synchronize()
-    err, ffn = check_y(np32(Y), OracleRun(inp).Y(), np32(inp.A), cfg.dtype)
+    err, ffn, _ = check_layer_output(layer, inp, Y)
     say(f"  rel err {err:.3e}, expert sum {ffn:.3e}")

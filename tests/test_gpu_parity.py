@@ -1,16 +1,23 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
-Bit-exact: router logits, top-k ids, slot counts and offsets, records
-(rec_token, rec_route), route_pos, n_valid. Tolerance: route weights alpha
-(relative 1e-6: expf and the softmax sum order differ), layer output
-max|y - y_ref| / max|y_ref| <= 1e-2 for bf16 layers and 1e-5 for the fp32
-layer. Inputs are the seeded synthetic workloads of inputs.py.
+Router logits: within the error bound of the GPU router's fp32 evaluation
+order of the oracle's correctly rounded logits (gpu_util.router_bound), and
+bitwise run-to-run identical. Bit-exact on shared inputs: top-k ids from the
+same logits, slot counts and offsets, records (rec_token, rec_route),
+route_pos, n_valid. Whole layers (router on the GPU): ids bit-exact on every
+token whose top-k no logit error within the bound can change; near ties
+checked for a valid pick. Tolerance: route weights alpha (relative 1e-6 on
+shared logits: expf and the softmax sum order differ; plus what the measured
+logit difference moves them otherwise), layer output max|y - y_ref| /
+max|y_ref| <= 1e-2 for bf16 layers and 1e-5 for the fp32 layer. Inputs are
+the seeded synthetic workloads of inputs.py.
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_util import (OracleRun, TOL, check_descriptors, check_y, check_topk, gpu_inputs, np32, rel_err,
+from gpu_util import (OracleRun, TOL, check_descriptors, check_layer_output, check_logits,
+                      check_routing_from_gpu_logits, check_y, check_topk, gpu_inputs, gpu_logits, np32, rel_err,
                       say)
 from oracle import oracle as oracle_mod
 from routed_expert_ffn_top_amd import binding as B
@@ -47,19 +54,31 @@ def test_mfma_lane_layout():
     assert np.array_equal(out.cpu().numpy().reshape(32, 32), A @ Bm)
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "olmoe_t1024", "virt_olmoe_t256", "mixtral_t256"])
-def test_router_logits_bitexact(name):
+@pytest.mark.parametrize("name", ["tiny_fp32", "olmoe_t1024", "olmoe_t4096", "virt_olmoe_t256", "mixtral_t256"])
+def test_router_logits_within_bound(name):
+    """GPU logits within the bound of the oracle's correctly rounded ones, the
+    same bits on a second call, and the top-k of the GPU logits equal to the
+    oracle's wherever no logit error within the bound can change it."""
     cfg = CONFIGS[name]
     if name == "mixtral_t256":
         cfg = cfg.with_(T=96, f=64)  # router only: keep the expert weights small
     say("router", name)
     inp = gpu_inputs(cfg)
-    s = B.make_shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.n_shared, dtype=cfg.dtype)
+    s = B.make_shape(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.n_shared, dtype=cfg.dtype, renorm=cfg.renorm)
     L = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
-    B.moe_router_logits(s, inp.X, inp.Wr.t().contiguous(), inp.bias, L)
+    Wr = inp.Wr.t().contiguous()
+    B.moe_router_logits(s, inp.X, Wr, inp.bias, L)
+    L2 = torch.empty_like(L)
+    B.moe_router_logits(s, inp.X, Wr, inp.bias, L2)
     torch.cuda.synchronize()
-    orc = OracleRun(inp)
-    assert np.array_equal(L.cpu().numpy().view(np.int32), orc.L.view(np.int32))
+    assert torch.equal(L.view(torch.int32), L2.view(torch.int32)), "router not run-to-run identical"
+    orun = OracleRun(inp)
+    Lg = L.cpu().numpy()
+    routes = B.alloc_routes(s)
+    ws = B.alloc_workspace(s)
+    B.moe_route_build(s, 0, cfg.T, L, list(range(cfg.n_exp)), 0, routes, ws)
+    torch.cuda.synchronize()
+    check_routing_from_gpu_logits(routes, orun, Lg)
 
 
 # (T, d, E, dtype, ldx): ragged token counts, d not a multiple of the 64-wide
@@ -78,7 +97,7 @@ ROUTER_SHAPES = [
 
 
 @pytest.mark.parametrize("T,d,E,dtype,ldx", ROUTER_SHAPES)
-def test_router_logits_shapes(T, d, E, dtype, ldx):
+def test_router_logits_shapes_within_bound(T, d, E, dtype, ldx):
     say("router shape", T, d, E, dtype, ldx)
     cfg = MoEConfig(name="router_shape", index=77, T=T, d=d, f=64, E=E, k=1, dtype=dtype)
     inp = make_inputs(cfg, device="cpu")
@@ -89,8 +108,7 @@ def test_router_logits_shapes(T, d, E, dtype, ldx):
     B.moe_router_logits(s, Xp.cuda(), inp.Wr.t().contiguous().cuda(), inp.bias.cuda() if inp.bias is not None
                         else None, L)
     torch.cuda.synchronize()
-    ref = oracle_mod.get().router_logits(np32(inp.X), np32(inp.Wr), None if inp.bias is None else np32(inp.bias))
-    assert np.array_equal(L.cpu().numpy().view(np.int32), ref.view(np.int32))
+    check_logits(L.cpu().numpy(), OracleRun(inp))
 
 
 ROUTE_CASES = {
@@ -187,14 +205,7 @@ def _check_layer(cfg, tokens=None, simple=False, repeats=3, **layer_kw):
     torch.cuda.synchronize()
     for r, Yr in enumerate(outs[1:], 1):
         assert torch.equal(Yr.view(torch.int32), Y.view(torch.int32)), f"run {r} differs from the last run"
-    orun = OracleRun(inp)
-    check_topk(layer.routes, orun)
-    if layer.shape.capacity >= cfg.T * cfg.kp and not layer.paged:
-        ref = orun.route_map(layer.phi, layer.shape.P)
-        check_descriptors(layer.routes, ref, n_valid_expected=cfg.T * cfg.kp)
-    toks = np.arange(cfg.T) if tokens is None else tokens
-    yref = orun.Y(tokens=toks)
-    err, ffn = check_y(np32(Y)[toks], yref, np32(inp.A)[toks], cfg.dtype)
+    err, ffn, _ = check_layer_output(layer, inp, Y, tokens=tokens)
     say(f"  {cfg.name}: rel err {err:.3e}, expert sum {ffn:.3e}")
     return Y, layer, inp
 
@@ -297,6 +308,8 @@ def test_partial_phi_leaves_out_absent_experts():
                      B.MOE_FFN_EXPERTS | B.MOE_FFN_FINALIZE, layer.ws)
     torch.cuda.synchronize()
     orun = OracleRun(inp)
+    same = check_routing_from_gpu_logits(layer.routes, orun, L.cpu().numpy())
+    assert same.all(), "near-tie picks: the partial map's records would differ"
     mask = np.isin(orun.idx, [1, 4, 9], invert=True).reshape(-1).astype(np.uint8)
     ref = orun.route_map(phi, s.P)
     check_descriptors(layer.routes, ref)
@@ -322,9 +335,7 @@ def test_paged_equals_resident():
     assert torch.equal(y2, y_res)
     counts = np.bincount(paged.routes["topk_idx"].cpu().numpy().reshape(-1), minlength=cfg.E)
     say(f"  experts with no routes: {int((counts == 0).sum())}")
-    orun = OracleRun(inp)
-    toks = np.arange(cfg.T)
-    check_y(np32(Y)[toks], orun.Y(tokens=toks), np32(inp.A)[toks], "bf16")
+    check_layer_output(paged, inp, Y)
 
 
 def test_edge_shapes():

@@ -15,18 +15,18 @@ import oracle_pins
 from oracle import oracle as oracle_mod
 
 MUTANTS = [
-    ("router drops the bias", "if (bias) s = s + bias[e];", ""),
-    ("router reads W_r transposed", "Wr[i * E + e], p[c]", "Wr[e * d + i], p[c]"),
-    ("router chains run in descending order", "for (int64_t i = 0; i < d; ++i) {\n                const int c",
-     "for (int64_t i = d - 1; i >= 0; --i) {\n                const int c"),
-    ("router rounds each product", "p[c] = fmaf(X[t * ldx + i], Wr[i * E + e], p[c]);",
-     "p[c] = p[c] + X[t * ldx + i] * Wr[i * E + e];"),
-    ("router adds the partial sums in descending order",
-     "float s = p[0];\n            for (int c = 1; c < 16; ++c) s = s + p[c];",
-     "float s = p[15];\n            for (int c = 14; c >= 0; --c) s = s + p[c];"),
-    ("router runs are 4 long", "(int)((i >> 3) & 15)", "(int)((i >> 2) & 15)"),
-    ("router has 8 partial sums", "(int)((i >> 3) & 15)", "(int)((i >> 3) & 7)"),
-    ("router is one chain", "(int)((i >> 3) & 15)", "0"),
+    ("router drops the bias", "if (bias) s += (double)bias[e];", ""),
+    ("router reads W_r transposed", "(double)Wr[i * E + e]", "(double)Wr[e * d + i]"),
+    ("router accumulates in fp32", "double s = 0.0;\n            for (int64_t i = 0; i < d; ++i)",
+     "float s = 0.0f;\n            for (int64_t i = 0; i < d; ++i)"),
+    ("router rounds each product to fp32", "s += (double)X[t * ldx + i] * (double)Wr[i * E + e];",
+     "s += (double)(X[t * ldx + i] * Wr[i * E + e]);"),
+    ("router rounds the dot product before the bias",
+     "if (bias) s += (double)bias[e];\n            L[t * E + e] = (float)s;",
+     "L[t * E + e] = (float)s;\n            if (bias) L[t * E + e] += bias[e];"),
+    ("router skips the last hidden index", "for (int64_t i = 0; i < d; ++i)\n                s +=",
+     "for (int64_t i = 0; i + 1 < d; ++i)\n                s +="),
+    ("router subtracts the bias", "if (bias) s += (double)bias[e];", "if (bias) s -= (double)bias[e];"),
     ("top-k ties go to the higher id", "l[e] > l[best]", "l[e] >= l[best]"),
     ("renormalisation inverted", "renorm ? (sel > 0.0 ? a / sel : 0.0) : a", "renorm ? a : (sel > 0.0 ? a / sel : 0.0)"),
     ("NaN logits not read as -infinity", "isnan(L[t * E + e]) ? -INFINITY : L[t * E + e]", "L[t * E + e]"),
