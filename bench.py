@@ -10,15 +10,23 @@ the pages; no trained weights).
 
 Prints one JSON line: routed tokens/s (T / layer time), the % of the bf16
 MFMA peak the layer reaches on its algorithmic FLOPs, a roofline entry for
-the dominant kernel (the gate/up projection) timed with HIP events around
-its own launches inside the timed region, and the CPU oracle's throughput on
-a bounded sample of the same workload.
+the dominant kernel (the gate/up projection), and the CPU oracle's throughput
+on a bounded sample of the same workload (all host cores and one core).
 
     python bench.py [--steps K] [--warmup W] [--workload olmoe_t4096]
 
-The default warm-up (60 steps, about 40 ms at OLMoE T=4096) covers the GPU's
-clock ramp: the first ~40 back-to-back layers run about 10 % slower than the
-steady state that the timed steps measure.
+Order of the run:
+  1. warm-up: W layers, continued until --warmup-min-s seconds have passed,
+     so that the timed steps run at steady clocks (the GPU's clocks ramp over
+     the first few tens of back-to-back layers); the first 20 warm-up layers
+     are timed one by one and reported, which shows the ramp;
+  2. the timed region: K layers between two events, nothing else recorded;
+  3. a second pass of K layers with one event between consecutive layers:
+     median, p10, p90, first and last step;
+  4. a third pass of K layers with every gate/up launch bracketed by HIP
+     events on its stream: the roofline's kernel time;
+  5. a per-kernel breakdown pass (every launch bracketed);
+  6. the CPU oracle.
 """
 from __future__ import annotations
 
@@ -66,6 +74,37 @@ for _n in list(WORKLOAD_TEXT):
                                    + "; expert weights stored as MXFP4 (E2M1 codes, one E8M0 scale per 32 "
                                    "weights of a row; weight-only quantisation, decoded to bf16 MFMA operands)")
 PCIE_GEN5_X16_GBS = 64.0   # one direction, before protocol overhead
+MALL_BYTES = 256 << 20     # MI355X Infinity Cache
+
+
+def working_set_bytes(cfg) -> int:
+    """Bytes one layer touches: expert weights, X, Y, and the intermediate H
+    and per-route rows Yr."""
+    esz = 4 if cfg.dtype == "f32" else 2
+    R = cfg.T * cfg.kp
+    return (cfg.n_exp * expert_slice_bytes(cfg) + cfg.T * cfg.d * (esz + 4) + R * cfg.f * esz + R * cfg.d * 4)
+
+
+def cold_cache_steps(torch, layer, Y, K, scratch_bytes=512 << 20) -> dict:
+    """Layer time with caches cold: before each layer a 512 MB scratch buffer
+    is written (twice the 256 MB Infinity Cache), then the layer alone is
+    timed between two events. For working sets that fit in the cache."""
+    import numpy as np
+    scratch = torch.empty(scratch_bytes // 4, dtype=torch.float32, device="cuda")
+    times = []
+    for i in range(K + 2):
+        scratch.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        layer.forward(Y)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(a.elapsed_time(b))
+    del scratch
+    return {"median_ms": round(float(np.median(times)), 4), "p10_ms": round(float(np.percentile(times, 10)), 4),
+            "p90_ms": round(float(np.percentile(times, 90)), 4), "steps": K,
+            "method": "512 MB scratch write before each layer, layer timed alone"}
 
 
 def gemm_source_hash() -> str:
@@ -298,10 +337,11 @@ def expert_slice_bytes(cfg) -> int:
     return 3 * cfg.d * cfg.f * (4 if cfg.dtype == "f32" else 2)
 
 
-def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
-    """The CPU oracle (as it stands) on the same workload: routing for every
-    token, the expert FFN on a token sample sized to ~target_s seconds,
-    extrapolated to the whole layer."""
+def cpu_baseline(inp, cfg, target_s=12.0, one_core_s=6.0) -> dict:
+    """The CPU oracle (as it stands) on the same workload, on all host cores
+    (OpenMP over tokens) and on one core: router, top-k and route map for the
+    tokens of the leg, then the expert FFN on a token sample sized to about
+    the leg's target seconds, extrapolated to the whole layer."""
     import numpy as np
     from oracle import oracle as oracle_mod
 
@@ -319,27 +359,43 @@ def cpu_baseline(inp, cfg, target_s=12.0) -> dict:
         Wg, Wu, Wd = dec(inp.Wg, inp.Sg), dec(inp.Wu, inp.Su), dec(inp.Wd, inp.Sd)
     else:
         Wg, Wu, Wd = f32(inp.Wg), f32(inp.Wu), f32(inp.Wd)
-    t0 = time.perf_counter()
-    L = orc.router_logits(X, Wr, bias)
-    idx, alpha = orc.topk(L, cfg.k, cfg.n_shared, cfg.renorm)
-    orc.route_map(idx, np.arange(cfg.n_exp, dtype=np.int32), cfg.n_exp)
-    t_route = time.perf_counter() - t0
-    probe = min(cfg.T, 16)
-    t1 = time.perf_counter()
-    orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, None, tokens=np.arange(probe), scales=scales)
-    per_tok = (time.perf_counter() - t1) / probe
-    n = int(min(cfg.T, max(probe, target_s / max(per_tok, 1e-9))))
-    rng = np.random.default_rng(5)
-    toks = np.sort(rng.choice(cfg.T, size=n, replace=False))
-    t2 = time.perf_counter()
-    orc.expert_ffn(X, idx, alpha, Wg, Wu, Wd, None, tokens=toks, scales=scales)
-    t_ffn = time.perf_counter() - t2
-    t_layer = t_route + t_ffn * cfg.T / n
-    return {"value": round(cfg.T / t_layer, 3), "unit": "tokens/s", "cores": orc.threads(),
+    all_threads = orc.threads()
+
+    def leg(threads, budget_s, route_tokens):
+        orc.set_threads(threads)
+        rt = np.arange(route_tokens)
+        t0 = time.perf_counter()
+        L = orc.router_logits(X[rt], Wr, bias)
+        idx, alpha = orc.topk(L, cfg.k, cfg.n_shared, cfg.renorm)
+        orc.route_map(idx, np.arange(cfg.n_exp, dtype=np.int32), cfg.n_exp)
+        t_route = (time.perf_counter() - t0) * cfg.T / route_tokens
+        idx_all, alpha_all = np.zeros((cfg.T, cfg.kp), np.int32), np.zeros((cfg.T, cfg.kp))
+        idx_all[rt], alpha_all[rt] = idx, alpha
+        probe = min(route_tokens, max(threads, 4))
+        t1 = time.perf_counter()
+        orc.expert_ffn(X, idx_all, alpha_all, Wg, Wu, Wd, None, tokens=np.arange(probe), scales=scales)
+        per_tok = (time.perf_counter() - t1) / probe
+        n = int(min(route_tokens, max(probe, budget_s / max(per_tok, 1e-9))))
+        rng = np.random.default_rng(5)
+        toks = np.sort(rng.choice(route_tokens, size=n, replace=False))
+        t2 = time.perf_counter()
+        orc.expert_ffn(X, idx_all, alpha_all, Wg, Wu, Wd, None, tokens=toks, scales=scales)
+        t_ffn = time.perf_counter() - t2
+        t_layer = t_route + t_ffn * cfg.T / n
+        return cfg.T / t_layer, t_route, n, t_ffn
+
+    v, t_route, n, t_ffn = leg(all_threads, target_s, cfg.T)
+    v1, t_route1, n1, t_ffn1 = leg(1, one_core_s, min(cfg.T, 256))
+    orc.set_threads(all_threads)
+    return {"value": round(v, 3), "unit": "tokens/s", "cores": all_threads,
             "kind": "oracle",
-            "sample": (f"router, top-k and route map for all {cfg.T} tokens ({t_route:.2f} s); expert FFN "
+            "sample": (f"{all_threads} threads: router, top-k and route map for all {cfg.T} tokens "
+                       f"({t_route:.2f} s); expert FFN "
                        + (f"for all {n} tokens ({t_ffn:.2f} s): the whole layer" if n == cfg.T else
-                          f"for {n} sampled tokens ({t_ffn:.2f} s), extrapolated to T={cfg.T}"))}
+                          f"for {n} sampled tokens ({t_ffn:.2f} s), extrapolated to T={cfg.T}")),
+            "one_core": {"value": round(v1, 3), "unit": "tokens/s", "cores": 1,
+                         "sample": (f"router, top-k and route map for {min(cfg.T, 256)} tokens and the expert FFN "
+                                    f"for {n1} of them ({t_ffn1:.2f} s), extrapolated to T={cfg.T}")}}
 
 
 def run_paged(args, cfg):
@@ -555,8 +611,12 @@ def bench_stack(args, cfg, n_layers: int = 32) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-min-s", type=float, default=1.0,
+                    help="keep warming up until this many seconds have passed (steady clocks)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time layers with a 512 MB scratch write before each (cold caches)")
     ap.add_argument("--workload", default="olmoe_t4096", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--group-size", type=int, default=None, help="paged workloads: experts per group")
@@ -589,6 +649,7 @@ def main() -> int:
                                    f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported"}))
         return 2
 
+    import numpy as np
     import torch
 
     from routed_expert_ffn_top_amd import binding as B
@@ -618,26 +679,54 @@ def main() -> int:
     inp = make_inputs(cfg, device="cuda", residual=False)
     layer = MoELayer(inp)
     Y = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
-    for _ in range(args.warmup):
-        layer.forward(Y)
-    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    K = args.steps
-    # timed region: K whole layers; the gate/up launches carry event pairs
-    B.moe_profile_begin("gate_up", K)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # 1. warm-up: W steps, and at least warmup_min_s seconds; the first 20
+    # steps are timed one by one (the clock ramp)
+    ramp = [ev() for _ in range(21)]
+    w_steps, w0 = 0, time.perf_counter()
+    while w_steps < args.warmup or time.perf_counter() - w0 < args.warmup_min_s:
+        if w_steps < 21:
+            ramp[w_steps].record()
+        layer.forward(Y)
+        w_steps += 1
+        if w_steps == 20:
+            ramp[20].record()
+        if w_steps % 20 == 0:
+            torch.cuda.synchronize()   # ties the wall-clock minimum to GPU time
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
+    warm_s = time.perf_counter() - w0
+    ramp_ms = [ramp[i].elapsed_time(ramp[i + 1]) for i in range(min(w_steps, 20))]
+
+    # 2. the timed region: K whole layers between two events
+    K = args.steps
+    start, stop = ev(), ev()
+    w1 = time.perf_counter()
     start.record()
     for _ in range(K):
         layer.forward(Y)
     stop.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    gate_up_ms = B.moe_profile_end("gate_up", K)
+    wall = time.perf_counter() - w1
     ms = start.elapsed_time(stop) / K
 
-    # per-kernel breakdown: a second pass with every kernel bracketed
+    # 3. per-step times: a second pass, one event between consecutive layers
+    marks = [ev() for _ in range(K + 1)]
+    marks[0].record()
+    for i in range(K):
+        layer.forward(Y)
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(K)])
+
+    # 4. gate/up launch times: a third pass, each launch bracketed on its stream
+    B.moe_profile_begin("gate_up", K)
+    for _ in range(K):
+        layer.forward(Y)
+    torch.cuda.synchronize()
+    gate_up_ms = B.moe_profile_end("gate_up", K)
+
+    # 5. per-kernel breakdown: every kernel bracketed
     names = ["router", "topk", "route_count", "route_place", "gate_up", "down", "combine"]
     reps = min(K, 10)
     for nme in names:
@@ -649,6 +738,10 @@ def main() -> int:
     for nme in names:
         d = B.moe_profile_end(nme, reps)
         breakdown[nme] = round(sum(d) / len(d), 4) if d else None
+
+    cold = None
+    if args.cold or working_set_bytes(cfg) < MALL_BYTES:
+        cold = cold_cache_steps(torch, layer, Y, K)
 
     R = cfg.T * cfg.kp
     flops_layer = 6.0 * R * cfg.d * cfg.f
@@ -684,6 +777,16 @@ def main() -> int:
         "kernel_ms": breakdown,
         "down_tflops": round(down_flops / (breakdown["down"] / 1e3) / 1e12, 1) if breakdown["down"] else None,
         "wall_s_timed": round(wall, 4),
+        "warmup_steps_run": w_steps,
+        "warmup_s": round(warm_s, 3),
+        "clock_ramp_ms": {"first_warmup_step": round(ramp_ms[0], 4) if ramp_ms else None,
+                          "warmup_steps_1_to_20_mean": round(float(np.mean(ramp_ms)), 4) if ramp_ms else None,
+                          "timed_mean": round(ms, 4)},
+        "step_ms": {"median": round(float(np.median(step_ms)), 4),
+                    "p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4),
+                    "first": round(float(step_ms[0]), 4), "last": round(float(step_ms[-1]), 4),
+                    "pass": f"second pass of {K} layers, one event between consecutive layers"},
         "roofline": {
             "kernel": "gate_up (gathered X rows x packed gate/up slice, bf16 MFMA, SwiGLU epilogue)",
             "bound": "mfma",
@@ -693,9 +796,13 @@ def main() -> int:
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "launch_ms_avg": round(gu_avg, 4),
+            "launch_timing": f"third pass of {K} layers after the timed region, each gate/up launch "
+                             "bracketed by HIP events on its own stream",
             "flops_per_launch": gate_up_flops,
         },
     }
+    if cold is not None:
+        out["cold_cache"] = cold
     if not args.no_context:
         out["context"] = {"torch_matmul_bf16_8192_tflops": round(torch_matmul_ceiling(torch), 1),
                           **torch_bmm_expert_shape(torch, cfg)}

@@ -115,7 +115,8 @@ typedef void *moe_stream; /* a hipStream_t */
  * routes; a build may place at most C routes, larger route sets are split
  * across invocations by token range).
  * Limits: 1 <= k <= E <= 256, k + n_shared <= 64, E + n_shared <= 512,
- * 1 <= P <= 512, T >= 0.
+ * 1 <= P <= 512, T >= 0, T * (k + n_shared) <= 2^30 - 1 routes,
+ * T * ceil(d / 1024) < 2^31 (MOE_ERR_UNSUPPORTED otherwise).
  * bf16 and bf16 with fp8 weights: d % 64 == 0, f % 64 == 0.
  * fp32: d % 4 == 0, f % 32 == 0.
  */
@@ -319,7 +320,7 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X,
  * slice whose rows alternate in blocks of 32: rows 64q..64q+31 are gate rows
  * 32q..32q+31 and rows 64q+32..64q+63 are up rows 32q..32q+31; that slice is
  * stored tiled. Down: W_d [d][f] stored tiled.
- * moe_pack_gate_up / moe_pack_down: device, n experts, source expert stride
+ * moe_pack_gate_up / moe_pack_down: device, n experts (0 <= n <= 65535), source expert stride
  * src_stride and destination stride dst_stride (elements; bytes for
  * MOE_DT_BF16_FP8W, whose source slices are row-major codes followed by one
  * fp32 scale per row, and whose packed slices keep their row scales after
@@ -371,9 +372,22 @@ moe_status arena_bind_slot(moe_arena *arena, int32_t slot, int32_t expert,
                            const void *src_gu, const void *src_d,
                            moe_stream copy_stream);
 
-/* Publish a slot whose contents the caller has written by other means
- * (e.g. moe_pack_gate_up into the plane) as holding `expert`; the ready
- * event is recorded on `stream` after that work. */
+/*
+ * Two-phase load for slices the caller writes by other means (e.g.
+ * moe_pack_gate_up into the plane), section 3.3: a binding is published only
+ * after the slot's gate, up and down slices are populated.
+ * arena_reserve_slot: Available/Ready/In-use -> Filling for `expert` (the
+ * slot's previous mapping is withdrawn; MOE_ERR_SLOT_STATE if the slot is
+ * already Filling or the expert occupies another slot). While Filling, the
+ * slot is in no placement map, a moe_expert_ffn whose phi names it fails
+ * with MOE_ERR_SLOT_STATE, and arena_bind_slot into it fails likewise. The
+ * caller must order its writes after the slot's last release itself (the
+ * library's own loads wait for it; writes issued by the caller do not).
+ * arena_publish_slot: Filling (reserved for `expert`) -> Ready; the ready
+ * event is recorded on `stream` after the caller's writes enqueued there. A
+ * slot that was not reserved is reserved and published in one step.
+ */
+moe_status arena_reserve_slot(moe_arena *arena, int32_t slot, int32_t expert);
 moe_status arena_publish_slot(moe_arena *arena, int32_t slot, int32_t expert,
                               moe_stream stream);
 

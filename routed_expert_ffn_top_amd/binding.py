@@ -87,6 +87,7 @@ _SIGS = {
     "moe_arena_create": ([_VP, _VP, _VP, _VP, _I64, _I64, _I32], _I32),
     "moe_arena_destroy": ([_VP], None),
     "arena_bind_slot": ([_VP, _I32, _I32, _VP, _VP, _VP], _I32),
+    "arena_reserve_slot": ([_VP, _I32, _I32], _I32),
     "arena_publish_slot": ([_VP, _I32, _I32, _VP], _I32),
     "arena_release_slot": ([_VP, _I32], _I32),
     "arena_phi": ([_VP, _VP, _I32], _I32),
@@ -263,6 +264,10 @@ def moe_arena_destroy(handle) -> None:
 def arena_bind_slot(arena, slot, expert, src_gu, src_d, copy_stream=None):
     _check(load().arena_bind_slot(arena.handle, slot, expert, _ptr(src_gu), _ptr(src_d),
                                   _stream(copy_stream)))
+
+
+def arena_reserve_slot(arena, slot, expert):
+    _check(load().arena_reserve_slot(arena.handle, slot, expert))
 
 
 def arena_publish_slot(arena, slot, expert, stream=None):

@@ -88,6 +88,10 @@ moe_status check_shape(const moe_shape *s)
     const int64_t routes = (int64_t)s->T * (s->k + s->n_shared);
     if (routes > INT32_MAX / 2 || (int64_t)s->capacity * s->f > (int64_t)1 << 40)
         return fail(MOE_ERR_UNSUPPORTED, "too many routes");
+    // the combine launches one workgroup per token and 1024 columns, on the
+    // grid's x dimension (at most 2^31 - 1 workgroups)
+    if ((int64_t)s->T * ((s->d / 4 + 255) / 256) > INT32_MAX)
+        return fail(MOE_ERR_UNSUPPORTED, "T * ceil(d / 1024) must be below 2^31");
     return MOE_OK;
 }
 
@@ -221,8 +225,10 @@ moe_status arena_reserve(moe_arena *a, int slot, int expert)
     if (slot < 0 || slot >= a->shape.P) return fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, P)", slot);
     if (expert < 0 || expert >= ne) return fail(MOE_ERR_INVALID_ARG, "expert %d outside [0, %d)", expert, ne);
     if (a->state[slot] == MOE_SLOT_FILLING) return fail(MOE_ERR_SLOT_STATE, "slot %d is Filling", slot);
-    if (a->slot_of[expert] >= 0 && a->slot_of[expert] != slot)
-        return fail(MOE_ERR_SLOT_STATE, "expert %d already occupies slot %d", expert, a->slot_of[expert]);
+    // the expert may hold (or be filling) no other slot
+    for (int s2 = 0; s2 < a->shape.P; ++s2)
+        if (s2 != slot && a->owner[s2] == expert)
+            return fail(MOE_ERR_SLOT_STATE, "expert %d already occupies slot %d", expert, s2);
     if (a->owner[slot] >= 0) a->slot_of[a->owner[slot]] = -1;  // withdraw the old mapping
     a->owner[slot] = expert;
     a->slot_of[expert] = -1;  // hidden while Filling
@@ -542,7 +548,7 @@ moe_status moe_pack_gate_up(const moe_shape *shape, const void *W_g, const void 
                             int64_t src_stride, int64_t dst_stride, moe_stream stream)
 {
     MOE_TRY(check_shape(shape));
-    if (!W_g || !W_u || !dst || n < 0) return fail(MOE_ERR_INVALID_ARG, "pack: bad arguments");
+    if (!W_g || !W_u || !dst || n < 0 || n > 65535) return fail(MOE_ERR_INVALID_ARG, "pack: bad arguments");
     const int esz = w_esz(*shape);
     const size_t src_bytes = src_slice_bytes(*shape, shape->f, shape->d);
     if (n > 1 && ((size_t)src_stride * esz < src_bytes || (size_t)dst_stride * esz < gu_slice_bytes(*shape)))
@@ -604,7 +610,7 @@ moe_status moe_pack_down(const moe_shape *shape, const void *W_d, void *dst, int
                          int64_t dst_stride, moe_stream stream)
 {
     MOE_TRY(check_shape(shape));
-    if (!W_d || !dst || n < 0) return fail(MOE_ERR_INVALID_ARG, "pack: bad arguments");
+    if (!W_d || !dst || n < 0 || n > 65535) return fail(MOE_ERR_INVALID_ARG, "pack: bad arguments");
     const int esz = w_esz(*shape);
     if (n > 1 && ((size_t)src_stride * esz < src_slice_bytes(*shape, shape->d, shape->f) ||
                   (size_t)dst_stride * esz < d_slice_bytes(*shape)))
@@ -690,11 +696,21 @@ moe_status arena_bind_slot(moe_arena *a, int32_t slot, int32_t expert, const voi
     return arena_bind_locked(a, slot, expert, src_gu, src_d, S(copy_stream));
 }
 
+moe_status arena_reserve_slot(moe_arena *a, int32_t slot, int32_t expert)
+{
+    if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
+    std::lock_guard<std::mutex> lk(a->mu);
+    return arena_reserve(a, slot, expert);
+}
+
 moe_status arena_publish_slot(moe_arena *a, int32_t slot, int32_t expert, moe_stream stream)
 {
     if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
     std::lock_guard<std::mutex> lk(a->mu);
-    MOE_TRY(arena_reserve(a, slot, expert));
+    if (slot < 0 || slot >= a->shape.P) return fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, P)", slot);
+    // a slot the caller reserved for this expert is published as it stands;
+    // any other slot is reserved first (Filling for another expert: refused)
+    if (!(a->state[slot] == MOE_SLOT_FILLING && a->owner[slot] == expert)) MOE_TRY(arena_reserve(a, slot, expert));
     moe_status rc = arena_events(a, slot);
     hipError_t e = rc == MOE_OK ? hipEventRecord(a->ready[slot], S(stream)) : hipSuccess;
     if (rc != MOE_OK || e != hipSuccess) {

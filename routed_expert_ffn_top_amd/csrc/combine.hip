@@ -30,10 +30,13 @@ template <int KP>
 __global__ __launch_bounds__(256) void k_combine(float *__restrict__ Y, int64_t ldy,
                                                  const float *__restrict__ Yr,
                                                  const int32_t *__restrict__ done, int d, int kp,
-                                                 int splits, int64_t split_stride)
+                                                 int splits, int64_t split_stride, int cblocks)
 {
-    const int t = blockIdx.y;
-    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    // one-dimensional grid: block b covers token b / cblocks, columns
+    // (b % cblocks) * 1024 .. +1023 (the x dimension holds any T this
+    // library accepts; the y dimension would cap it at 65535)
+    const int t = (int)(blockIdx.x / (unsigned)cblocks);
+    const int c = ((int)(blockIdx.x % (unsigned)cblocks) * 256 + threadIdx.x) * 4;
     if (c >= d) return;
     float4 y = *(const float4 *)(Y + (int64_t)t * ldy + c);
     if constexpr (KP > 0) {
@@ -180,11 +183,12 @@ hipError_t launch_combine(const moe_shape &s, float *Y, const float *Yr, const i
                           hipStream_t st)
 {
     if (s.T == 0) return hipSuccess;
-    const dim3 grid((unsigned)((s.d / 4 + 255) / 256), (unsigned)s.T);
+    const int cblocks = (s.d / 4 + 255) / 256;
+    const dim3 grid((unsigned)((int64_t)s.T * cblocks));
     const int kp = s.k + s.n_shared, splits = down_splits(s);
     const int64_t sstride = (int64_t)s.T * kp * s.d;
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, Y, s.ldy, Yr, done, s.d, kp, splits, sstride);
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, Y, s.ldy, Yr, done, s.d, kp, splits, sstride, cblocks);
     };
     if (splits == 1 && kp == 8)
         go(k_combine<8>);

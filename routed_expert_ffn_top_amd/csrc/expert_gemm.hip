@@ -855,9 +855,7 @@ hipError_t launch_simple(const GemmArgs &a, int max_rows, hipStream_t st)
 #ifndef MOE_RING_TILE
 #define MOE_RING_TILE 256, 256, 4, 4, 2
 #endif
-#ifndef MOE_DOWN_TILE
-#define MOE_DOWN_TILE MOE_RING_TILE
-#endif
+
 // MXFP4 weights: 2 wave rows x 4 wave columns, so that each weight fragment
 // is decoded by 2 waves instead of 4 (bf16 and fp8 measured slower so).
 #ifndef MOE_FP4_TILE
@@ -887,7 +885,7 @@ hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool
         return launch_simple<uint16_t, false>(a, max_rows, st);
     }
     if (a.bfp4) return launch_mfma_lds<MOE_FP4_TILE, false>(a, max_rows, st);
-    return launch_mfma_lds<MOE_DOWN_TILE, false>(a, max_rows, st);
+    return launch_mfma_lds<MOE_RING_TILE, false>(a, max_rows, st);
 }
 
 }  // namespace moe

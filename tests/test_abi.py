@@ -54,6 +54,7 @@ def test_version_and_error_channel():
     (dict(ldy=130), B.MOE_ERR_INVALID_ARG),
     (dict(f=96), B.MOE_ERR_UNSUPPORTED),
     (dict(ldx=132), B.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 24, d=1 << 17), B.MOE_ERR_UNSUPPORTED),   # T * ceil(d / 1024) = 2^31 combine workgroups
 ])
 def test_shape_checks(kw, status):
     base = dict(T=16, d=128, f=256, E=8, k=2, dtype="bf16")
@@ -401,3 +402,60 @@ def test_device_pack_rejects_misaligned_pointers(dtype):
     with pytest.raises(B.MoEError) as ei:
         B.moe_pack_down(s, 0x100002, 0x300000, 1, 0, 0, stream=0)
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
+
+
+def _fake_arena(P=4, E=4):
+    """An arena over fake plane addresses: the residency table lives on the
+    host, and the calls below are refused before any HIP call."""
+    s = B.make_shape(T=16, d=128, f=256, E=E, k=2, P=P, dtype="bf16")
+    h = B.moe_arena_create(s, 0x7f0000000000, 0x7f1000000000, 2 * 256 * 128, 128 * 256, P)
+
+    class _A:
+        handle = h
+    return s, _A()
+
+
+def test_residency_refusals_on_the_host():
+    """Section 3.3's protocol on the host side: a reserved (Filling) slot is
+    in no placement map and an FFN naming it is refused; a bind or a second
+    reservation into a Filling slot, a publication for another expert, an
+    expert mapped to two slots and a phi naming a slot that does not hold
+    its expert are refused; release returns a slot to Available."""
+    s, a = _fake_arena()
+    try:
+        B.arena_reserve_slot(a, 1, 2)
+        assert B.arena_slot_info(a, 1) == (B.MOE_SLOT_FILLING, 2)
+        assert B.arena_phi(a, 4) == [-1, -1, -1, -1]
+        ws = _FakeWs(B.moe_workspace_bytes(s))
+        r = _fake_routes(s)
+        with pytest.raises(B.MoEError) as ei:      # FFN over a Filling slot
+            B.moe_expert_ffn(s, 0x7f2000000000, None, r, a, [-1, -1, 1, -1], B.MOE_FFN_EXPERTS, ws, 0)
+        assert ei.value.status == B.MOE_ERR_SLOT_STATE
+        with pytest.raises(B.MoEError) as ei:      # FFN over an Available slot
+            B.moe_expert_ffn(s, 0x7f2000000000, None, r, a, [0, -1, -1, -1], B.MOE_FFN_EXPERTS, ws, 0)
+        assert ei.value.status == B.MOE_ERR_SLOT_STATE
+        with pytest.raises(B.MoEError) as ei:      # bind into a Filling slot
+            B.arena_bind_slot(a, 1, 3, 0x1000, 0x2000, 0)
+        assert ei.value.status == B.MOE_ERR_SLOT_STATE
+        with pytest.raises(B.MoEError) as ei:      # reserve a Filling slot again
+            B.arena_reserve_slot(a, 1, 3)
+        assert ei.value.status == B.MOE_ERR_SLOT_STATE
+        with pytest.raises(B.MoEError) as ei:      # publish a Filling slot for another expert
+            B.arena_publish_slot(a, 1, 3, 0)
+        assert ei.value.status == B.MOE_ERR_SLOT_STATE
+        with pytest.raises(B.MoEError) as ei:      # release a Filling slot
+            B.arena_release_slot(a, 1)
+        assert ei.value.status == B.MOE_ERR_SLOT_STATE
+        B.arena_reserve_slot(a, 0, 1)
+        with pytest.raises(B.MoEError) as ei:      # expert 1 is already in slot 0
+            B.arena_reserve_slot(a, 3, 1)
+        assert ei.value.status == B.MOE_ERR_SLOT_STATE
+        with pytest.raises(B.MoEError) as ei:      # slot and expert out of range
+            B.arena_reserve_slot(a, 4, 0)
+        assert ei.value.status == B.MOE_ERR_INVALID_ARG
+        with pytest.raises(B.MoEError) as ei:
+            B.arena_reserve_slot(a, 2, 4)
+        assert ei.value.status == B.MOE_ERR_INVALID_ARG
+        assert B.arena_slot_info(a, 2) == (B.MOE_SLOT_AVAILABLE, -1)
+    finally:
+        B.moe_arena_destroy(a.handle)

@@ -271,6 +271,11 @@ def test_layer_mixtral_t4096():
     _check_layer(CONFIGS["mixtral_t4096"], repeats=2)
 
 
+def test_layer_mixtral_t1024():
+    say("layer Mixtral T=1024 (one row block per expert, split-K down), every token")
+    _check_layer(CONFIGS["mixtral_t1024"], repeats=2)
+
+
 def test_layer_mixtral_t256():
     say("layer Mixtral T=256, every token")
     cfg = CONFIGS["mixtral_t256"]
