@@ -2,14 +2,14 @@
 // arena with its residency table, and the order of kernel launches.
 //
 // Residency table (EStream, section 3.3, "Bounded Parameter Arena and Safe
-// Slot Reuse"): a slot is Available, Filling (owner recorded, mapping hidden),
-// Ready (published) or In-use (submitted). On a GPU stream the protocol is
-// carried by two events per slot: "ready" is recorded on the copy stream
-// after the slot's slices are copied, and every invocation that reads the
-// slot waits for it; "release" is recorded on the compute stream after the
-// last invocation that reads the slot, and a later load into the slot waits
-// for it. So no invocation sees a partly loaded expert, and no load
-// overwrites a slot that queued work still reads, without any host wait.
+// Slot Reuse"): residency.h holds the states and the stream-ordered events
+// that carry the protocol; here it runs on HIP streams and events. "ready" is
+// recorded on the copy stream after a slot's slices are copied, and every
+// invocation that reads the slot waits for it; "release" is recorded on the
+// compute stream after the last invocation that reads the slot, and a later
+// load into the slot waits for it. So no invocation sees a partly loaded
+// expert, and no load overwrites a slot that queued work still reads,
+// without any host wait.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "common.h"
+#include "residency.h"
 
 using namespace moe;
 
@@ -184,77 +185,56 @@ void prof_end(int kid, int i, hipStream_t st)
 // ---------------------------------------------------------------------------
 // arena
 
+namespace {
+
+// Streams and events of the residency table: HIP's.
+struct HipBackend {
+    using Stream = hipStream_t;
+    using Event = hipEvent_t;
+    hipError_t last = hipSuccess;
+    int create(Event *e) { return (last = hipEventCreateWithFlags(e, hipEventDisableTiming)) != hipSuccess; }
+    void destroy(Event e) { (void)hipEventDestroy(e); }
+    int record(Event e, Stream s) { return (last = hipEventRecord(e, s)) != hipSuccess; }
+    int wait(Stream s, Event e) { return (last = hipStreamWaitEvent(s, e, 0)) != hipSuccess; }
+    int sync(Event e) { return (last = hipEventSynchronize(e)) != hipSuccess; }
+};
+
+}  // namespace
+
 struct moe_arena {
     std::mutex mu;
     moe_shape shape;
     char *plane_gu;
     char *plane_d;
-    int64_t stride_gu, stride_d;  // elements (bytes for fp8 weights)
+    int64_t stride_gu, stride_d;  // elements (bytes for quantised weights)
     int G;
     int esz;
-    std::vector<int> state, owner, slot_of;  // per slot, per slot, per expert
-    // "ready": one event per slot, recorded after the slot's load; a stream
-    // that already waited for the current record does not wait again.
-    std::vector<hipEvent_t> ready;
-    std::vector<uint64_t> ready_gen;
-    std::vector<hipStream_t> waited_stream;
-    std::vector<uint64_t> waited_gen;
-    // "release": each invocation records one event from a ring of kRing on its
-    // stream after its work; a slot remembers the ring entry of its last use,
-    // and a later load into the slot waits for it. Before a ring entry is
-    // recorded again its previous record is waited for on the host (it is
-    // kRing invocations old) and the slots that pointed at it are cleared.
-    static constexpr int kRing = 32;
-    std::vector<hipEvent_t> ring;
-    int ring_pos = 0;
-    std::vector<int> last_use;  // per slot: ring index or -1
+    HipBackend bk;
+    ResidencyTable<HipBackend> res;
+    moe_arena(const moe_shape &s) : shape(s), res(bk, s.P, s.E + s.n_shared) {}
 };
 
 namespace {
 
-moe_status arena_events(moe_arena *a, int slot)
+// Reports an error of the residency table through the library's error
+// channel (errors raised by the caller's own code have already been).
+moe_status R(moe_arena *a, moe_status st)
 {
-    if (!a->ready[slot]) HIP_TRY(hipEventCreateWithFlags(&a->ready[slot], hipEventDisableTiming), "hipEventCreate");
-    return MOE_OK;
+    if (st != MOE_OK && a->res.msg()[0]) {
+        if (st == MOE_ERR_HIP)
+            fail(st, "%s: %s", a->res.msg(), hipGetErrorString(a->bk.last));
+        else
+            fail(st, "%s", a->res.msg());
+        a->res.clear_msg();
+    }
+    return st;
 }
 
-// Available/Ready/In-use -> Filling for (slot, expert); caller holds the lock.
-moe_status arena_reserve(moe_arena *a, int slot, int expert)
-{
-    const int ne = a->shape.E + a->shape.n_shared;
-    if (slot < 0 || slot >= a->shape.P) return fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, P)", slot);
-    if (expert < 0 || expert >= ne) return fail(MOE_ERR_INVALID_ARG, "expert %d outside [0, %d)", expert, ne);
-    if (a->state[slot] == MOE_SLOT_FILLING) return fail(MOE_ERR_SLOT_STATE, "slot %d is Filling", slot);
-    // the expert may hold (or be filling) no other slot
-    for (int s2 = 0; s2 < a->shape.P; ++s2)
-        if (s2 != slot && a->owner[s2] == expert)
-            return fail(MOE_ERR_SLOT_STATE, "expert %d already occupies slot %d", expert, s2);
-    if (a->owner[slot] >= 0) a->slot_of[a->owner[slot]] = -1;  // withdraw the old mapping
-    a->owner[slot] = expert;
-    a->slot_of[expert] = -1;  // hidden while Filling
-    a->state[slot] = MOE_SLOT_FILLING;
-    return MOE_OK;
-}
-
-void arena_publish_locked(moe_arena *a, int slot)
-{
-    a->state[slot] = MOE_SLOT_READY;
-    a->slot_of[a->owner[slot]] = slot;
-}
-
-void arena_abort_fill(moe_arena *a, int slot)
-{
-    a->owner[slot] = -1;
-    a->state[slot] = MOE_SLOT_AVAILABLE;
-}
-
-// Binds expert ex[i] to slot sl[i] for i < n, with loads on `st`: every slot
-// goes Filling, the stream waits for each slot's last release, the copies
-// run, and each slot's ready event is recorded and the slot published.
-// Neighbouring entries whose slots are consecutive and whose prepacked host
-// slices follow each other in memory are copied with one transfer per plane.
-// With `timed`, the copies (not the waits) are bracketed for
-// moe_profile_begin(MOE_KERNEL_H2D). Caller holds the lock.
+// Binds expert ex[i] to slot sl[i] for i < n, with loads on `st` (see
+// ResidencyTable::load). Neighbouring entries whose slots are consecutive
+// and whose prepacked host slices follow each other in memory are copied
+// with one transfer per plane. With `timed`, the copies (not the waits) are
+// bracketed for moe_profile_begin(MOE_KERNEL_H2D). Caller holds the lock.
 moe_status arena_bind_many_locked(moe_arena *a, const int *sl, const int *ex, int n, const void *const *src_gu,
                                   const void *const *src_d, hipStream_t st, bool timed)
 {
@@ -265,44 +245,26 @@ moe_status arena_bind_many_locked(moe_arena *a, const int *sl, const int *ex, in
     const bool packed_planes = (size_t)a->stride_gu * a->esz == gu_bytes && (size_t)a->stride_d * a->esz == d_bytes;
     for (int i = 0; i < n; ++i)
         if (!src_gu[i] || !src_d[i]) return fail(MOE_ERR_INVALID_ARG, "bind source is NULL");
-    int reserved = 0;
-    moe_status rc = MOE_OK;
-    while (reserved < n) {
-        rc = arena_reserve(a, sl[reserved], ex[reserved]);
-        if (rc != MOE_OK) break;
-        ++reserved;
-        rc = arena_events(a, sl[reserved - 1]);
-        if (rc != MOE_OK) break;
-    }
-    hipError_t e = hipSuccess;
-    for (int i = 0; i < n && rc == MOE_OK && e == hipSuccess; ++i)
-        if (a->last_use[sl[i]] >= 0) e = hipStreamWaitEvent(st, a->ring[a->last_use[sl[i]]], 0);
-    const int pi = (rc == MOE_OK && e == hipSuccess && timed) ? prof_begin(MOE_KERNEL_H2D, st) : -1;
-    for (int i = 0; i < n && rc == MOE_OK && e == hipSuccess;) {
-        int j = i + 1;   // extend while slots are consecutive and host slices contiguous
-        while (packed_planes && j < n && sl[j] == sl[j - 1] + 1 &&
-               (const char *)src_gu[j] == (const char *)src_gu[j - 1] + gu_bytes &&
-               (const char *)src_d[j] == (const char *)src_d[j - 1] + d_bytes)
-            ++j;
-        e = hipMemcpyAsync(a->plane_gu + (size_t)sl[i] * a->stride_gu * a->esz, src_gu[i],
-                           gu_bytes * (size_t)(j - i), hipMemcpyDefault, st);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(a->plane_d + (size_t)sl[i] * a->stride_d * a->esz, src_d[i],
-                               d_bytes * (size_t)(j - i), hipMemcpyDefault, st);
-        i = j;
-    }
-    if (pi >= 0) prof_end(MOE_KERNEL_H2D, pi, st);
-    for (int i = 0; i < n && rc == MOE_OK && e == hipSuccess; ++i) e = hipEventRecord(a->ready[sl[i]], st);
-    if (rc != MOE_OK || e != hipSuccess) {
-        for (int i = 0; i < reserved; ++i)
-            if (a->state[sl[i]] == MOE_SLOT_FILLING) arena_abort_fill(a, sl[i]);
-        return rc != MOE_OK ? rc : hip_fail(e, "arena bind");
-    }
-    for (int i = 0; i < n; ++i) {
-        a->ready_gen[sl[i]] += 1;
-        arena_publish_locked(a, sl[i]);
-    }
-    return MOE_OK;
+    auto write = [&](hipStream_t cs) -> moe_status {
+        const int pi = timed ? prof_begin(MOE_KERNEL_H2D, cs) : -1;
+        hipError_t e = hipSuccess;
+        for (int i = 0; i < n && e == hipSuccess;) {
+            int j = i + 1;   // extend while slots are consecutive and host slices contiguous
+            while (packed_planes && j < n && sl[j] == sl[j - 1] + 1 &&
+                   (const char *)src_gu[j] == (const char *)src_gu[j - 1] + gu_bytes &&
+                   (const char *)src_d[j] == (const char *)src_d[j - 1] + d_bytes)
+                ++j;
+            e = hipMemcpyAsync(a->plane_gu + (size_t)sl[i] * a->stride_gu * a->esz, src_gu[i],
+                               gu_bytes * (size_t)(j - i), hipMemcpyDefault, cs);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(a->plane_d + (size_t)sl[i] * a->stride_d * a->esz, src_d[i],
+                                   d_bytes * (size_t)(j - i), hipMemcpyDefault, cs);
+            i = j;
+        }
+        if (pi >= 0) prof_end(MOE_KERNEL_H2D, pi, cs);
+        return e == hipSuccess ? MOE_OK : hip_fail(e, "arena bind copy");
+    };
+    return R(a, a->res.load(sl, ex, n, st, write));
 }
 
 moe_status arena_bind_locked(moe_arena *a, int slot, int expert, const void *src_gu, const void *src_d,
@@ -314,43 +276,12 @@ moe_status arena_bind_locked(moe_arena *a, int slot, int expert, const void *src
 // Checks phi against the arena, makes `st` wait for each named slot's load.
 moe_status arena_acquire(moe_arena *a, const int32_t *phi, hipStream_t st)
 {
-    const int ne = a->shape.E + a->shape.n_shared;
-    for (int e = 0; e < ne; ++e) {
-        const int s = phi[e];
-        if (s < 0) continue;
-        if ((a->state[s] != MOE_SLOT_READY && a->state[s] != MOE_SLOT_IN_USE) || a->owner[s] != e)
-            return fail(MOE_ERR_SLOT_STATE, "phi maps expert %d to slot %d, which is not Ready with it", e, s);
-    }
-    for (int e = 0; e < ne; ++e) {
-        const int s = phi[e];
-        if (s < 0 || (a->waited_stream[s] == st && a->waited_gen[s] == a->ready_gen[s])) continue;
-        HIP_TRY(hipStreamWaitEvent(st, a->ready[s], 0), "hipStreamWaitEvent");
-        a->waited_stream[s] = st;
-        a->waited_gen[s] = a->ready_gen[s];
-    }
-    return MOE_OK;
+    return R(a, a->res.acquire(phi, st));
 }
 
 moe_status arena_release_after(moe_arena *a, const int32_t *phi, hipStream_t st)
 {
-    const int ne = a->shape.E + a->shape.n_shared;
-    const int pos = a->ring_pos;
-    if (!a->ring[pos]) {
-        HIP_TRY(hipEventCreateWithFlags(&a->ring[pos], hipEventDisableTiming), "hipEventCreate");
-    } else {
-        HIP_TRY(hipEventSynchronize(a->ring[pos]), "hipEventSynchronize");
-        for (int s = 0; s < a->shape.P; ++s)
-            if (a->last_use[s] == pos) a->last_use[s] = -1;
-    }
-    HIP_TRY(hipEventRecord(a->ring[pos], st), "hipEventRecord");
-    a->ring_pos = (pos + 1) % moe_arena::kRing;
-    for (int e = 0; e < ne; ++e) {
-        const int s = phi[e];
-        if (s < 0) continue;
-        a->last_use[s] = pos;
-        a->state[s] = MOE_SLOT_IN_USE;
-    }
-    return MOE_OK;
+    return R(a, a->res.release_after(phi, st));
 }
 
 // ---------------------------------------------------------------------------
@@ -657,35 +588,20 @@ moe_status moe_arena_create(moe_arena **out, const moe_shape *shape, void *plane
         return fail(MOE_ERR_INVALID_ARG, "need 1 <= G <= P and P %% G == 0");
     if (!aligned(plane_gu, 16) || !aligned(plane_d, 16) || (stride_gu * esz) % 16 || (stride_d * esz) % 16)
         return fail(MOE_ERR_INVALID_ARG, "planes and slot strides must be 16-byte aligned");
-    moe_arena *a = new moe_arena();
-    a->shape = *shape;
+    moe_arena *a = new moe_arena(*shape);
     a->plane_gu = (char *)plane_gu;
     a->plane_d = (char *)plane_d;
     a->stride_gu = stride_gu;
     a->stride_d = stride_d;
     a->G = G;
     a->esz = esz;
-    a->state.assign(shape->P, MOE_SLOT_AVAILABLE);
-    a->owner.assign(shape->P, -1);
-    a->slot_of.assign(shape->E + shape->n_shared, -1);
-    a->ready.assign(shape->P, nullptr);
-    a->ready_gen.assign(shape->P, 0);
-    a->waited_stream.assign(shape->P, nullptr);
-    a->waited_gen.assign(shape->P, 0);
-    a->ring.assign(moe_arena::kRing, nullptr);
-    a->last_use.assign(shape->P, -1);
     *out = a;
     return MOE_OK;
 }
 
 void moe_arena_destroy(moe_arena *a)
 {
-    if (!a) return;
-    for (auto e : a->ready)
-        if (e) (void)hipEventDestroy(e);
-    for (auto e : a->ring)
-        if (e) (void)hipEventDestroy(e);
-    delete a;
+    delete a;   // the residency table destroys its events
 }
 
 moe_status arena_bind_slot(moe_arena *a, int32_t slot, int32_t expert, const void *src_gu, const void *src_d,
@@ -700,38 +616,21 @@ moe_status arena_reserve_slot(moe_arena *a, int32_t slot, int32_t expert)
 {
     if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
     std::lock_guard<std::mutex> lk(a->mu);
-    return arena_reserve(a, slot, expert);
+    return R(a, a->res.reserve(slot, expert));
 }
 
 moe_status arena_publish_slot(moe_arena *a, int32_t slot, int32_t expert, moe_stream stream)
 {
     if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
     std::lock_guard<std::mutex> lk(a->mu);
-    if (slot < 0 || slot >= a->shape.P) return fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, P)", slot);
-    // a slot the caller reserved for this expert is published as it stands;
-    // any other slot is reserved first (Filling for another expert: refused)
-    if (!(a->state[slot] == MOE_SLOT_FILLING && a->owner[slot] == expert)) MOE_TRY(arena_reserve(a, slot, expert));
-    moe_status rc = arena_events(a, slot);
-    hipError_t e = rc == MOE_OK ? hipEventRecord(a->ready[slot], S(stream)) : hipSuccess;
-    if (rc != MOE_OK || e != hipSuccess) {
-        arena_abort_fill(a, slot);
-        return rc != MOE_OK ? rc : hip_fail(e, "arena_publish_slot");
-    }
-    a->ready_gen[slot] += 1;
-    arena_publish_locked(a, slot);
-    return MOE_OK;
+    return R(a, a->res.publish(slot, expert, S(stream)));
 }
 
 moe_status arena_release_slot(moe_arena *a, int32_t slot)
 {
     if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
     std::lock_guard<std::mutex> lk(a->mu);
-    if (slot < 0 || slot >= a->shape.P) return fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, P)", slot);
-    if (a->state[slot] == MOE_SLOT_FILLING) return fail(MOE_ERR_SLOT_STATE, "slot %d is Filling", slot);
-    if (a->owner[slot] >= 0) a->slot_of[a->owner[slot]] = -1;
-    a->owner[slot] = -1;
-    a->state[slot] = MOE_SLOT_AVAILABLE;
-    return MOE_OK;
+    return R(a, a->res.release(slot));
 }
 
 moe_status arena_phi(const moe_arena *a, int32_t *phi, int32_t n)
@@ -739,9 +638,7 @@ moe_status arena_phi(const moe_arena *a, int32_t *phi, int32_t n)
     if (!a || !phi) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
     const int ne = a->shape.E + a->shape.n_shared;
     if (n < ne) return fail(MOE_ERR_INVALID_ARG, "phi needs %d entries", ne);
-    for (int e = 0; e < n; ++e) phi[e] = -1;
-    for (int s = 0; s < a->shape.P; ++s)
-        if (a->state[s] == MOE_SLOT_READY || a->state[s] == MOE_SLOT_IN_USE) phi[a->owner[s]] = s;
+    a->res.placement(phi, n);
     return MOE_OK;
 }
 
@@ -749,8 +646,8 @@ moe_status arena_slot_info(const moe_arena *a, int32_t slot, int32_t *state, int
 {
     if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
     if (slot < 0 || slot >= a->shape.P) return fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, P)", slot);
-    if (state) *state = a->state[slot];
-    if (expert) *expert = a->owner[slot];
+    if (state) *state = a->res.state(slot);
+    if (expert) *expert = a->res.owner(slot);
     return MOE_OK;
 }
 
@@ -867,11 +764,7 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float 
     const int ngroups = (ne + G - 1) / G;
     const int npre = std::min(B, ngroups);
     std::lock_guard<std::mutex> lk(arena->mu);
-    for (int sl = 0; sl < s.P; ++sl) {  // forget the previous layer's mapping
-        if (arena->owner[sl] >= 0) arena->slot_of[arena->owner[sl]] = -1;
-        arena->owner[sl] = -1;
-        arena->state[sl] = MOE_SLOT_AVAILABLE;
-    }
+    arena->res.forget_mapping();   // the previous layer's experts are gone
     std::vector<int> bsl, bex;
     std::vector<const void *> bgu, bd;
     auto bind_group = [&](int g, int bank, const int32_t *counts) -> moe_status {
