@@ -302,6 +302,33 @@ moe_status moe_layer_prefill(const moe_shape *shape, const void *X,
                              moe_stream copy);
 
 /*
+ * moe_layer_prefill_noalloc -- for callers that cannot allocate memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). The resident layer of moe_layer_prefill (host_gu = host_d =
+ * NULL, no copy stream), with the same arguments, checks, kernels and
+ * results (bit for bit), except that its workspace is a fixed device array
+ * inside this library instead of a caller buffer, and it calls no
+ * allocating routine (no hipMalloc or hipFree; the arena must already have
+ * been loaded, so no event is created either).
+ *   Limit: shapes whose moe_workspace_bytes exceeds 64 MiB (67108864 bytes)
+ *   are refused with MOE_ERR_WORKSPACE before any GPU work: T <= 815 tokens
+ *   for the OLMoE-shaped layer (d = 2048, f = 1024, top-8), T <= 759 for the
+ *   DeepSeek-V2-Lite-shaped one, T <= 356 for the Mixtral-shaped one.
+ *   Each GPU the library runs on holds its own 64 MiB array until the
+ *   process ends. Every call on a GPU uses that GPU's array and finds the
+ *   previous call's contents; the device error word is cleared at the start
+ *   of each call. Calls that overlap on one GPU (other streams or threads)
+ *   race on the array and must be serialized by the caller. Device errors
+ *   cannot arise here (routing is computed by the call itself).
+ */
+moe_status moe_layer_prefill_noalloc(const moe_shape *shape, const void *X,
+                                     const float *W_r, const float *bias,
+                                     const float *logits, float *Y,
+                                     moe_arena *arena,
+                                     const moe_routes *routes,
+                                     moe_stream stream);
+
+/*
  * Weight packing (section 3.3, "Offline NPU-Consumable Weight Layout":
  * experts are stored in the layout the kernels consume).
  *

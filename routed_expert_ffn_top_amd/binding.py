@@ -80,6 +80,7 @@ _SIGS = {
     "moe_route_build": ([_VP, _I32, _I32, _VP, _VP, _I32, _VP, _VP, _SZ, _VP], _I32),
     "moe_expert_ffn": ([_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _SZ, _VP], _I32),
     "moe_layer_prefill": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP, _VP], _I32),
+    "moe_layer_prefill_noalloc": ([_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP], _I32),
     "moe_pack_gate_up": ([_VP, _VP, _VP, _VP, _I32, _I64, _I64, _VP], _I32),
     "moe_pack_gate_up_host": ([_VP, _VP, _VP, _VP], _I32),
     "moe_pack_down": ([_VP, _VP, _VP, _I32, _I64, _I64, _VP], _I32),
@@ -230,6 +231,12 @@ def moe_layer_prefill(shape, X, W_r, bias, logits, Y, arena, host_gu, host_d, ro
                                     _ptr(Y), arena.handle, gu, d, ctypes.byref(rs), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(compute),
                                     _stream(copy) if copy is not None else None))
+
+
+def moe_layer_prefill_noalloc(shape, X, W_r, bias, logits, Y, arena, routes: dict, stream=None):
+    rs = routes_struct(routes)
+    _check(load().moe_layer_prefill_noalloc(ctypes.byref(shape), _ptr(X), _ptr(W_r), _ptr(bias), _ptr(logits),
+                                            _ptr(Y), arena.handle, ctypes.byref(rs), _stream(stream)))
 
 
 def moe_pack_gate_up(shape, Wg, Wu, dst, n, src_stride, dst_stride, stream=None):

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_gfx950.so")
-SOURCES = ["router.hip", "route_map.hip", "expert_gemm.hip", "combine.hip", "api.cpp"]
+SOURCES = ["router.hip", "route_map.hip", "expert_gemm.hip", "combine.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -118,7 +118,8 @@ moe_status check_phi(const moe_shape *s, const int32_t *phi, PhiArg *out)
 {
     if (!phi) return fail(MOE_ERR_INVALID_ARG, "phi is NULL");
     const int ne = s->E + s->n_shared;
-    std::vector<int> used(s->P, -1);
+    int used[kMaxExp];   // on the stack: the allocation-free entry point runs this too
+    for (int q = 0; q < s->P; ++q) used[q] = -1;
     for (int e = 0; e < ne; ++e) {
         const int v = phi[e];
         if (v < -1 || v >= s->P) return fail(MOE_ERR_INVALID_ARG, "phi[%d] = %d outside [-1, P)", e, v);
@@ -691,59 +692,96 @@ moe_status moe_selftest_mfma_layout(float *out, moe_stream stream)
     return MOE_OK;
 }
 
-moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float *W_r, const float *bias,
-                             const float *logits, float *Y, moe_arena *arena, const void *const *host_gu,
-                             const void *const *host_d, const moe_routes *routes, void *ws, size_t ws_bytes,
-                             moe_stream compute, moe_stream copy)
+}  // extern "C"
+
+namespace moe {
+
+moe_status report_error(moe_status st, const char *msg) { return fail(st, "%s", msg); }
+
+// Checks shared by the layer calls; on success *w is the workspace layout.
+static moe_status layer_checks(const moe_shape *shape, const void *X, const float *W_r, const float *logits,
+                               float *Y, moe_arena *arena, const moe_routes *routes, void *ws, size_t ws_bytes,
+                               WsLayout *w)
 {
-    MOE_TRY(check_shape(shape));
-    if (shape->T == 0) return MOE_OK;  // an empty prompt: nothing to do
     MOE_TRY(check_routes(routes));
-    WsLayout w;
-    MOE_TRY(check_ws(shape, ws, ws_bytes, &w));
+    MOE_TRY(check_ws(shape, ws, ws_bytes, w));
     if (!X || !Y || !arena) return fail(MOE_ERR_INVALID_ARG, "layer: X, Y and arena are required");
     if (!W_r && !logits) return fail(MOE_ERR_INVALID_ARG, "layer: give W_r or logits");
     if (W_r) MOE_TRY(check_router_args(shape, X, W_r));
     if (!aligned(Y, 16) || (act_bf16(*shape) && !aligned(X, 16)))
         return fail(MOE_ERR_INVALID_ARG, "layer: X and Y must be 16-byte aligned");
-    if ((host_gu == nullptr) != (host_d == nullptr))
-        return fail(MOE_ERR_INVALID_ARG, "layer: give both host_gu and host_d, or neither");
     if (arena->shape.d != shape->d || arena->shape.f != shape->f || arena->shape.P != shape->P ||
         arena->shape.dtype != shape->dtype || arena->shape.E != shape->E || arena->shape.n_shared != shape->n_shared)
         return fail(MOE_ERR_INVALID_ARG, "arena was made for another shape");
+    return MOE_OK;
+}
+
+// The resident layer (every expert Ready in the arena): router, then per
+// capacity-sized token range a route build and the expert FFN, then the
+// combine. Host state lives on the stack. With clear_err, the workspace's
+// device error word is cleared first (by a kernel).
+moe_status layer_prefill_resident(const moe_shape *shape, const void *X, const float *W_r, const float *bias,
+                                  const float *logits, float *Y, moe_arena *arena, const moe_routes *routes,
+                                  void *ws, size_t ws_bytes, hipStream_t cs, bool clear_err)
+{
+    MOE_TRY(check_shape(shape));
+    if (shape->T == 0) return MOE_OK;  // an empty prompt: nothing to do
+    WsLayout w;
+    MOE_TRY(layer_checks(shape, X, W_r, logits, Y, arena, routes, ws, ws_bytes, &w));
+    const moe_shape &s = *shape;
+    const int kp = s.k + s.n_shared, ne = s.E + s.n_shared;
+    const float *L = logits;
+    int32_t phi[kMaxExp];
+    PhiArg pa;
+    if (clear_err) HIP_TRY(launch_fill_i32(ws_at<int32_t>(ws, w.err), 0, 64, cs), "fill launch");
+    if (W_r) {
+        L = ws_at<float>(ws, w.logits);
+        HIP_TRY(TIMED(MOE_KERNEL_ROUTER, cs, launch_router_logits(s, X, W_r, bias, ws_at<float>(ws, w.logits), cs)),
+                "router launch");
+    }
+    // every expert must be Ready in the arena
+    MOE_TRY(arena_phi(arena, phi, ne));
+    for (int e = 0; e < ne; ++e)
+        if (phi[e] < 0) return fail(MOE_ERR_SLOT_STATE, "expert %d is not resident", e);
+    MOE_TRY(check_phi(shape, phi, &pa));
+    const int tc = (int)std::min<int64_t>(s.T, s.capacity / kp);
+    if (s.T > 0 && tc < 1) return fail(MOE_ERR_CAPACITY, "capacity %d below one token's %d routes", s.capacity, kp);
+    std::lock_guard<std::mutex> lk(arena->mu);
+    MOE_TRY(arena_acquire(arena, phi, cs));
+    for (int t0 = 0; t0 < s.T; t0 += tc) {
+        const int nt = std::min(tc, s.T - t0);
+        MOE_TRY(route_build_impl(s, w, t0, nt, L, pa, MOE_ROUTE_RESET, *routes, ws, cs));
+        MOE_TRY(experts_impl(s, w, X, *routes, arena, nt * kp, false, ws, cs));
+    }
+    MOE_TRY(arena_release_after(arena, phi, cs));
+    HIP_TRY(TIMED(MOE_KERNEL_COMBINE, cs, launch_combine(s, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), cs)),
+            "combine launch");
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_layer_prefill(const moe_shape *shape, const void *X, const float *W_r, const float *bias,
+                             const float *logits, float *Y, moe_arena *arena, const void *const *host_gu,
+                             const void *const *host_d, const moe_routes *routes, void *ws, size_t ws_bytes,
+                             moe_stream compute, moe_stream copy)
+{
+    if ((host_gu == nullptr) != (host_d == nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "layer: give both host_gu and host_d, or neither");
+    if (!host_gu)
+        return layer_prefill_resident(shape, X, W_r, bias, logits, Y, arena, routes, ws, ws_bytes, S(compute), false);
+    MOE_TRY(check_shape(shape));
+    if (shape->T == 0) return MOE_OK;  // an empty prompt: nothing to do
+    WsLayout w;
+    MOE_TRY(layer_checks(shape, X, W_r, logits, Y, arena, routes, ws, ws_bytes, &w));
     const moe_shape &s = *shape;
     const int kp = s.k + s.n_shared, ne = s.E + s.n_shared;
     hipStream_t cs = S(compute), ps = copy ? S(copy) : cs;
     const float *L = logits;
     std::vector<int32_t> phi(kMaxExp, -1);
     PhiArg pa;
-
-    if (!host_gu) {
-        if (W_r) {
-            L = ws_at<float>(ws, w.logits);
-            HIP_TRY(TIMED(MOE_KERNEL_ROUTER, cs,
-                          launch_router_logits(s, X, W_r, bias, ws_at<float>(ws, w.logits), cs)),
-                    "router launch");
-        }
-        // Resident layer: every expert must be Ready in the arena.
-        MOE_TRY(arena_phi(arena, phi.data(), ne));
-        for (int e = 0; e < ne; ++e)
-            if (phi[e] < 0) return fail(MOE_ERR_SLOT_STATE, "expert %d is not resident", e);
-        MOE_TRY(check_phi(shape, phi.data(), &pa));
-        const int tc = (int)std::min<int64_t>(s.T, s.capacity / kp);
-        if (s.T > 0 && tc < 1) return fail(MOE_ERR_CAPACITY, "capacity %d below one token's %d routes", s.capacity, kp);
-        std::lock_guard<std::mutex> lk(arena->mu);
-        MOE_TRY(arena_acquire(arena, phi.data(), cs));
-        for (int t0 = 0; t0 < s.T; t0 += tc) {
-            const int nt = std::min(tc, s.T - t0);
-            MOE_TRY(route_build_impl(s, w, t0, nt, L, pa, MOE_ROUTE_RESET, *routes, ws, cs));
-            MOE_TRY(experts_impl(s, w, X, *routes, arena, nt * kp, false, ws, cs));
-        }
-        MOE_TRY(arena_release_after(arena, phi.data(), cs));
-        HIP_TRY(TIMED(MOE_KERNEL_COMBINE, cs, launch_combine(s, Y, ws_at<float>(ws, w.Yr), ws_at<int32_t>(ws, w.done), cs)),
-                "combine launch");
-        return MOE_OK;
-    }
 
     // Paged layer (sections 3.3-3.4). Group g holds experts g*G .. g*G+G-1
     // (expert e is member r(e) = e mod G; the permutation pi is the

@@ -177,6 +177,16 @@ hipError_t launch_pack_gate_up(const moe_shape &s, const void *Wg, const void *W
 hipError_t launch_pack_down(const moe_shape &s, const void *Wd, void *dst, int n, int64_t src_stride,
                             int64_t dst_stride, hipStream_t st);
 hipError_t launch_selftest_mfma(float *out, hipStream_t st);
+
+// Stores a message in the library's error channel (moe_last_error) and
+// returns st.
+moe_status report_error(moe_status st, const char *msg);
+// The resident layer of moe_layer_prefill on a given workspace (all argument
+// checks included); with clear_err the workspace's device error word is
+// cleared by a kernel first. No host or device memory is allocated.
+moe_status layer_prefill_resident(const moe_shape *shape, const void *X, const float *W_r, const float *bias,
+                                  const float *logits, float *Y, moe_arena *arena, const moe_routes *routes,
+                                  void *ws, size_t ws_bytes, hipStream_t cs, bool clear_err);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, int64_t n, hipStream_t st);
 hipError_t launch_expert_hist(const moe_shape &s, const int32_t *idx, int64_t n, int32_t *count,
                               hipStream_t st);

@@ -100,8 +100,10 @@ public:
         moe_status rc = MOE_OK;
         while (reserved < n && rc == MOE_OK) {
             rc = reserve(sl[reserved], ex[reserved]);
-            if (rc == MOE_OK) rc = ensure_ready_event(sl[reserved++]);
+            if (rc == MOE_OK) ++reserved;
         }
+        if (rc == MOE_OK) rc = ensure_ring();
+        for (int i = 0; i < n && rc == MOE_OK; ++i) rc = ensure_ready_event(sl[i]);
         for (int i = 0; i < n && rc == MOE_OK; ++i)
             if (last_use_[sl[i]] >= 0 && bk_.wait(st, ring_[last_use_[sl[i]]]))
                 rc = err(MOE_ERR_HIP, "wait for slot %d's release", sl[i]);
@@ -127,7 +129,8 @@ public:
             const moe_status rc = reserve(slot, expert);
             if (rc != MOE_OK) return rc;
         }
-        moe_status rc = ensure_ready_event(slot);
+        moe_status rc = ensure_ring();
+        if (rc == MOE_OK) rc = ensure_ready_event(slot);
         if (rc == MOE_OK && bk_.record(ready_[slot], st)) rc = err(MOE_ERR_HIP, "record slot %d's ready event", slot);
         if (rc != MOE_OK) {
             abort_fill(slot);
@@ -158,7 +161,9 @@ public:
     }
 
     // After an invocation's work on st: record a release event and mark the
-    // slots phi names In-use with it as their last use.
+    // slots phi names In-use with it as their last use. The ring's events are
+    // created by the first load or publication, so an invocation (whose slots
+    // must have been loaded) creates none.
     moe_status release_after(const int32_t *phi, Stream st)
     {
         const int pos = ring_pos_;
@@ -211,6 +216,15 @@ public:
     }
 
 private:
+    moe_status ensure_ring()
+    {
+        for (int i = 0; i < kRing; ++i) {
+            if (ring_set_[i]) continue;
+            if (bk_.create(&ring_[i])) return err(MOE_ERR_HIP, "create a release event");
+            ring_set_[i] = 1;
+        }
+        return MOE_OK;
+    }
     moe_status ensure_ready_event(int slot)
     {
         if (has_ready_[slot]) return MOE_OK;

@@ -459,3 +459,23 @@ def test_residency_refusals_on_the_host():
         assert B.arena_slot_info(a, 2) == (B.MOE_SLOT_AVAILABLE, -1)
     finally:
         B.moe_arena_destroy(a.handle)
+
+
+def test_noalloc_refusals_on_the_host():
+    """The allocation-free layer refuses, before any GPU work, a shape whose
+    workspace exceeds its fixed 64 MiB device array, and an invalid shape
+    with the shape check's own status."""
+    s, a = _fake_arena()
+    try:
+        big = B.make_shape(T=4096, d=2048, f=1024, E=64, k=8, dtype="bf16")
+        assert B.moe_workspace_bytes(big) > 64 << 20
+        r = _fake_routes(big)
+        with pytest.raises(B.MoEError) as ei:
+            B.moe_layer_prefill_noalloc(big, 0x7f2000000000, 0x7f3000000000, None, None, 0x7f4000000000, a, r, 0)
+        assert ei.value.status == B.MOE_ERR_WORKSPACE and "67108864" in str(ei.value)
+        bad = B.make_shape(T=16, d=100, f=256, E=8, k=2, dtype="bf16")
+        with pytest.raises(B.MoEError) as ei:
+            B.moe_layer_prefill_noalloc(bad, 0x7f2000000000, 0x7f3000000000, None, None, 0x7f4000000000, a, r, 0)
+        assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "d % 64" in str(ei.value)
+    finally:
+        B.moe_arena_destroy(a.handle)
