@@ -551,6 +551,78 @@ def bench_configure(args, cfg, sizes=(1, 2, 4, 8, 16)) -> int:
     return 0
 
 
+def bench_fused(args, cfg) -> int:
+    """The fused expert tile (MOE_FFN_FUSED: gate/up, SwiGLU and down in one
+    kernel, H kept in LDS) against the two projection kernels on the same
+    layer: each path runs router, route build, expert FFN and combine as
+    separate calls; per-kernel HIP events and whole-step times over K steps
+    after a time-based warm-up."""
+    import numpy as np
+    import torch
+
+    from routed_expert_ffn_top_amd import binding as B
+    from routed_expert_ffn_top_amd.inputs import make_inputs
+    from routed_expert_ffn_top_amd.layer import MoELayer
+
+    inp = make_inputs(cfg, device="cuda", residual=False)
+    layer = MoELayer(inp)
+    s = layer.shape
+    Y = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    L = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+
+    def step(fused):
+        B.moe_router_logits(s, layer.X, layer.Wr, layer.bias, L)
+        B.moe_route_build(s, 0, s.T, L, layer.phi, 0, layer.routes, layer.ws)
+        fl = B.MOE_FFN_EXPERTS | B.MOE_FFN_FINALIZE | (B.MOE_FFN_FUSED if fused else 0)
+        B.moe_expert_ffn(s, layer.X, Y, layer.routes, layer.arena, layer.phi, fl, layer.ws)
+
+    K = args.steps
+    res = {}
+    for fused in (False, True):
+        w0 = time.perf_counter()
+        n = 0
+        while n < args.warmup or time.perf_counter() - w0 < args.warmup_min_s:
+            step(fused)
+            n += 1
+            if n % 20 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            step(fused)
+        b.record()
+        torch.cuda.synchronize()
+        names = ["fused"] if fused else ["gate_up", "down"]
+        for nme in names + ["combine"]:
+            B.moe_profile_begin(nme, K)
+        for _ in range(K):
+            step(fused)
+        torch.cuda.synchronize()
+        kern = {nme: round(float(np.mean(B.moe_profile_end(nme, K))), 4) for nme in names + ["combine"]}
+        res["fused" if fused else "split"] = {"step_ms": round(a.elapsed_time(b) / K, 4), "kernel_ms": kern}
+    R = cfg.T * cfg.kp
+    flops = 6.0 * R * cfg.d * cfg.f
+    sp = res["split"]["kernel_ms"]
+    ffn_split = sp["gate_up"] + sp["down"]
+    ffn_fused = res["fused"]["kernel_ms"]["fused"]
+    out = {
+        "metric": "expert FFN time: fused expert tile vs the two projection kernels (1 GPU)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "f": cfg.f},
+        "steps": K,
+        "split": res["split"],
+        "fused": res["fused"],
+        "expert_ffn_ms": {"split": round(ffn_split, 4), "fused": round(ffn_fused, 4)},
+        "expert_ffn_tflops": {"split": round(flops / (ffn_split / 1e3) / 1e12, 1),
+                              "fused": round(flops / (ffn_fused / 1e3) / 1e12, 1)},
+        "fused_over_split": round(ffn_fused / ffn_split, 3),
+    }
+    print(json.dumps(out), flush=True)
+    layer.close()
+    return 0
+
+
 def bench_stack(args, cfg, n_layers: int = 32) -> int:
     """A stack of n_layers MoE layers with independent weights (each layer's
     own seeded X, router and experts), all resident in HBM; one step runs the
@@ -615,6 +687,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--warmup-min-s", type=float, default=1.0,
                     help="keep warming up until this many seconds have passed (steady clocks)")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the fused expert tile against the two projection kernels")
     ap.add_argument("--cold", action="store_true",
                     help="also time layers with a 512 MB scratch write before each (cold caches)")
     ap.add_argument("--workload", default="olmoe_t4096", choices=sorted(WORKLOAD_TEXT))
@@ -675,6 +749,8 @@ def main() -> int:
         return bench_paged(args, CONFIGS[args.workload])
     if args.workload.startswith("mixtral_stack_"):
         return bench_stack(args, CONFIGS[args.workload.replace("mixtral_stack_", "mixtral_")])
+    if args.fused:
+        return bench_fused(args, CONFIGS[args.workload])
     cfg = CONFIGS[args.workload]
     inp = make_inputs(cfg, device="cuda", residual=False)
     layer = MoELayer(inp)

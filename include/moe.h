@@ -99,6 +99,12 @@ typedef void *moe_stream; /* a hipStream_t */
                                    MFMA kernel (an independent second path);
                                    MOE_ERR_UNSUPPORTED with fp8 or MXFP4
                                    weights */
+#define MOE_FFN_FUSED 8 /* bf16 weights: one fused kernel per 64-record tile
+                           runs gate/up, SwiGLU and down with H kept on chip
+                           (section 3.2, fused expert execution); the same
+                           bits as the two projection kernels. Needs f <= 1024,
+                           d % 128 == 0 and an unsplit down projection (see
+                           moe_expert_ffn), MOE_ERR_UNSUPPORTED otherwise. */
 
 /* Residency states (section 3.3, "Bounded Parameter Arena and Safe Slot Reuse") */
 #define MOE_SLOT_AVAILABLE 0
@@ -260,7 +266,7 @@ moe_status moe_route_build(const moe_shape *shape, int32_t t0, int32_t nt,
  *          (MOE_ERR_SLOT_STATE otherwise); the stream waits for each such
  *          slot's load, and each slot's release is recorded after the work.
  *   flags  MOE_FFN_EXPERTS and/or MOE_FFN_FINALIZE (and optionally
- *          MOE_FFN_SIMPLE_KERNEL).
+ *          MOE_FFN_SIMPLE_KERNEL or MOE_FFN_FUSED).
  * MOE_FFN_EXPERTS: for each record p of slot s, H[p] = SiLU(g) * u with
  * (g, u) = X[rec_token[p]] times slot s's gate/up slice, then
  * Yr[rec_route[p]] = alpha * (H[p] times slot s's down slice); the route is
@@ -449,7 +455,8 @@ moe_status moe_selftest_mfma_layout(float *out, moe_stream stream);
 #define MOE_KERNEL_DOWN 6
 #define MOE_KERNEL_COMBINE 7
 #define MOE_KERNEL_H2D 8        /* the two host-to-device copies of one bind */
-#define MOE_KERNEL_COUNT 9
+#define MOE_KERNEL_FUSED 9      /* the fused expert kernel (MOE_FFN_FUSED) */
+#define MOE_KERNEL_COUNT 10
 /* moe_profile_begin arms timing of one kernel id for the next max_launches
  * launches (process-wide): each such launch is bracketed by a pair of HIP
  * events recorded on the launch's stream. moe_profile_end waits for those

@@ -43,6 +43,7 @@ MOE_ROUTE_RESET = 1
 MOE_FFN_EXPERTS = 1
 MOE_FFN_FINALIZE = 2
 MOE_FFN_SIMPLE_KERNEL = 4
+MOE_FFN_FUSED = 8
 MOE_SLOT_AVAILABLE, MOE_SLOT_FILLING, MOE_SLOT_READY, MOE_SLOT_IN_USE = 0, 1, 2, 3
 MOE_MAX_EXPERTS = 512
 
@@ -99,7 +100,7 @@ _SIGS = {
 }
 
 MOE_KERNEL = {"router": 1, "topk": 2, "route_count": 3, "route_place": 4, "gate_up": 5, "down": 6,
-              "combine": 7, "h2d": 8}
+              "combine": 7, "h2d": 8, "fused": 9}
 
 
 def lib_path() -> str:

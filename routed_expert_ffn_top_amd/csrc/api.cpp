@@ -327,10 +327,13 @@ GemmArgs gemm_args(const moe_shape &s, const moe_routes &r, const moe_arena *a)
 }
 
 moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, const moe_routes &r,
-                        moe_arena *a, int max_rows, bool simple, void *ws, hipStream_t st)
+                        moe_arena *a, int max_rows, bool simple, void *ws, hipStream_t st, bool fused = false)
 {
     if (simple && (w_fp8(s) || w_fp4(s)))
         return fail(MOE_ERR_UNSUPPORTED, "the plain kernel reads bf16 or fp32 weights only");
+    if (fused && (simple || !fused_expert_supported(s)))
+        return fail(MOE_ERR_UNSUPPORTED, "the fused expert kernel needs bf16 weights, f <= 1024, d %% 128 == 0 "
+                                         "and an unsplit down projection");
     GemmArgs g = gemm_args(s, r, a);
     g.A = X;
     g.lda = s.ldx;
@@ -343,7 +346,7 @@ moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, co
     g.K = s.d;
     g.C = ws_at<char>(ws, w.H);
     g.ldc = s.f;
-    HIP_TRY(TIMED(MOE_KERNEL_GATE_UP, st, launch_gate_up(s, g, max_rows, simple, st)), "gate/up launch");
+    if (!fused) HIP_TRY(TIMED(MOE_KERNEL_GATE_UP, st, launch_gate_up(s, g, max_rows, simple, st)), "gate/up launch");
     GemmArgs h = gemm_args(s, r, a);
     h.A = ws_at<char>(ws, w.H);
     h.lda = s.f;
@@ -359,6 +362,10 @@ moe_status experts_impl(const moe_shape &s, const WsLayout &w, const void *X, co
     h.done = ws_at<int32_t>(ws, w.done);
     h.splits = down_splits(s);
     h.split_stride = (int64_t)s.T * (s.k + s.n_shared) * s.d;
+    if (fused) {
+        HIP_TRY(TIMED(MOE_KERNEL_FUSED, st, launch_fused_expert(s, g, h, max_rows, st)), "fused expert launch");
+        return MOE_OK;
+    }
     HIP_TRY(TIMED(MOE_KERNEL_DOWN, st, launch_down(s, h, max_rows, simple, st)), "down launch");
     return MOE_OK;
 }
@@ -464,7 +471,7 @@ moe_status moe_expert_ffn(const moe_shape *shape, const void *X, float *Y, const
         MOE_TRY(arena_acquire(arena, phi, S(stream)));
         const int max_rows = std::min<int64_t>(shape->capacity, (int64_t)shape->T * (shape->k + shape->n_shared));
         MOE_TRY(experts_impl(*shape, w, X, *routes, arena, max_rows, (flags & MOE_FFN_SIMPLE_KERNEL) != 0, ws,
-                             S(stream)));
+                             S(stream), (flags & MOE_FFN_FUSED) != 0));
         MOE_TRY(arena_release_after(arena, phi, S(stream)));
     }
     if (flags & MOE_FFN_FINALIZE) {

@@ -170,6 +170,11 @@ hipError_t launch_gate_up(const moe_shape &s, const GemmArgs &a, int max_rows, b
                           hipStream_t st);
 hipError_t launch_down(const moe_shape &s, const GemmArgs &a, int max_rows, bool simple,
                        hipStream_t st);
+// Fused expert tile (gate/up, SwiGLU and down in one kernel, H kept in LDS):
+// bf16 layers with f <= 1024, d % 128 == 0 and an unsplit down projection.
+bool fused_expert_supported(const moe_shape &s);
+hipError_t launch_fused_expert(const moe_shape &s, const GemmArgs &gu, const GemmArgs &dn, int max_rows,
+                               hipStream_t st);
 hipError_t launch_combine(const moe_shape &s, float *Y, const float *Yr, const int32_t *done,
                           hipStream_t st);   // sums the down_splits(s) partial rows of each route
 hipError_t launch_pack_gate_up(const moe_shape &s, const void *Wg, const void *Wu, void *dst,

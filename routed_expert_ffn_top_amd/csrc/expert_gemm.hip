@@ -838,6 +838,206 @@ hipError_t launch_mfma_lds(const GemmArgs &a, int max_rows, hipStream_t st)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Fused expert tile (section 3.2, "Fused Expert Execution with Intra-NPU
+// Pipelining": the SwiGLU output stays on chip until the down projection
+// consumes it). One workgroup takes FBM = 64 records of one slot through both
+// projections:
+//   phase 1: H = SiLU(X W_g^T) * (X W_u^T) for all f hidden units, 128 packed
+//            gate/up columns (64 hidden units) per pass over K = d, written
+//            to LDS as bf16 (64 x f x 2 bytes, at most 128 KB);
+//   phase 2: out = H W_d^T, 128 output columns per pass over K = f, with H
+//            read from LDS; alpha * out goes to the route's row of Yr, as the
+//            split down kernel writes it.
+// Both phases run the split kernels' MFMA instruction over the same k order
+// with the same fragments, and H is rounded to bf16 the same way, so the
+// results equal theirs bit for bit; H just never goes to HBM. Operands
+// stream through a 2-stage LDS ring (12 KB per stage: 64 gathered X rows and
+// 128 weight rows of one 32-wide K piece in phase 1, 128 weight rows in phase
+// 2); 4 waves, each 32 rows x 64 columns. H in LDS is stored like a ring
+// stage per K piece of 32 hidden units (64 rows of 64 bytes, 16-byte chunks
+// XOR-swizzled by row), so phase 2 reads its A fragments the way the ring
+// kernels read a stage. Tiles are numbered slot by slot and dealt to the
+// XCDs in contiguous ranges, as in the split kernels.
+constexpr int FBM = 64, FNT = 256, FMAXF = 1024;
+
+__global__ __launch_bounds__(FNT, 1) void k_fused_expert(GemmArgs g, GemmArgs dn, int max_tiles)
+{
+    constexpr int BK = 32, ROWB = 64, STAGE = FBM * ROWB + 128 * ROWB;   // 12 KB
+    constexpr int HPIECE = FBM * ROWB;                                     // 4 KB per 32 hidden units
+    __shared__ __attribute__((aligned(1024))) char hs[FMAXF / BK * HPIECE];
+    __shared__ __attribute__((aligned(1024))) char ring[2 * STAGE];
+    __shared__ int32_t s_route[FBM];
+    __shared__ float s_alpha[FBM];
+    __shared__ int32_t s_tpref[kGemmMaxSlots + 1];
+    __shared__ int32_t s_off[kGemmMaxSlots + 1];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rh = wave >> 1, ch = wave & 1;    // 32-row half, 64-column half
+    const int P = g.P, d = g.K, f = dn.K;
+    if (tid < 64) {
+        int run = 0;
+        for (int s0 = 0; s0 < P; s0 += 64) {
+            const int s = s0 + lane;
+            const int off = s < P ? g.slot_offset[s] : 0;
+            const int cnt = s < P ? g.slot_offset[s + 1] - off : 0;
+            const int w = (cnt + FBM - 1) / FBM;
+            const int inc = wave_incl_scan(w, lane);
+            if (s < P) {
+                s_tpref[s] = run + inc - w;
+                s_off[s] = off;
+            }
+            run += __shfl(inc, 63, 64);
+        }
+        if (lane == 0) {
+            s_tpref[P] = run;
+            s_off[P] = g.slot_offset[P];
+        }
+    }
+    __syncthreads();
+    const int total = min(s_tpref[P], max_tiles);
+    const int xcd = blockIdx.x % kXcd, li = blockIdx.x / kXcd;
+    const int nwg = ((int)gridDim.x - xcd + kXcd - 1) / kXcd;
+    const int qx = total / kXcd, rx = total % kXcd;
+    const int cnt_x = qx + (xcd < rx ? 1 : 0), start_x = xcd * qx + min(xcd, rx);
+
+    const int lr = lane >> 2, lp = lane & 3;
+    const int sw = ((lane & 31) >> 2) & 3;
+    const int foff[2] = {(lane & 31) * ROWB + ((0 + (lane >> 5)) ^ sw) * 16,
+                         (lane & 31) * ROWB + ((2 + (lane >> 5)) ^ sw) * 16};
+    const int nk1 = d / BK, nk2 = f / BK;
+    const int n1 = (2 * f / 128) * nk1, n2 = (d / 128) * nk2;
+
+    for (int tl = li; tl < cnt_x; tl += nwg) {
+        const int L = start_x + tl;
+        int lo = 0, hi = P - 1;   // last slot whose first tile is <= L
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_tpref[mid] <= L) lo = mid; else hi = mid - 1;
+        }
+        const int slot = lo;
+        const int row0 = s_off[slot] + (L - s_tpref[slot]) * FBM;
+        const int rows = __builtin_amdgcn_readfirstlane(min(FBM, s_off[slot + 1] - row0));
+        __syncthreads();   // every wave is done with the previous tile's route entries
+        if (tid < FBM) {
+            const int rt = dn.rec_route[row0 + min(tid, rows - 1)];
+            s_route[tid] = rt;
+            s_alpha[tid] = dn.topk_w[rt];
+        }
+        // this lane's gathered X row (A rows 16 wave + lane / 4) and its chunk
+        const int ar = wave * 16 + lr;
+        const char *xrow = (const char *)g.A + (int64_t)g.rec_token[row0 + min(ar, rows - 1)] * g.lda * 2 +
+                           (lp ^ ((ar >> 2) & 3)) * 16;
+        const char *gslot = (const char *)g.B + (int64_t)slot * g.slot_stride * 2;
+        const char *dslot = (const char *)dn.B + (int64_t)slot * dn.slot_stride * 2;
+        // B copies: rows 32 wave + 16 j + lane / 4 of a 128-row weight stage
+        auto bsrc = [&](const char *sl, int N, int K, int n0, int kt, int j) {
+            const int r = wave * 32 + j * 16 + lr;
+            const int nb = n0 / kWRows, rows_nb = min(kWRows, N - nb * kWRows);
+            return sl + ((int64_t)nb * kWRows * K + (int64_t)kt * rows_nb * BK + (int64_t)(n0 % kWRows + r) * BK) * 2 +
+                   (lp ^ ((r >> 2) & 3)) * 16;
+        };
+        auto issue1 = [&](int st) {
+            const int cb = st / nk1, kt = st % nk1;
+            char *stg = ring + (st & 1) * STAGE;
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)(xrow + (int64_t)kt * BK * 2),
+                                             (LDS_AS void *)(stg + wave * 1024), 16, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)bsrc(gslot, g.N, d, cb * 128, kt, j),
+                                                 (LDS_AS void *)(stg + FBM * ROWB + (wave * 2 + j) * 1024), 16, 0,
+                                                 0);
+        };
+        auto issue2 = [&](int st) {
+            const int nb2 = st / nk2, kt = st % nk2;
+            char *stg = ring + (st & 1) * STAGE;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                __builtin_amdgcn_global_load_lds((const GLOBAL_AS void *)bsrc(dslot, dn.N, f, nb2 * 128, kt, j),
+                                                 (LDS_AS void *)(stg + (wave * 2 + j) * 1024), 16, 0, 0);
+        };
+
+        f32x16_t acc[2];
+        // phase 1: gate/up pairs and SwiGLU into LDS
+        __syncthreads();   // the previous tile is done with the ring and the route entries are in
+        issue1(0);
+        for (int st = 0; st < n1; ++st) {
+            const int cb = st / nk1, kt = st % nk1;
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (st + 1 < n1) issue1(st + 1);
+            if (kt == 0)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+            const char *stg = ring + (st & 1) * STAGE;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8_t a = *(const bf16x8_t *)(stg + rh * 32 * ROWB + foff[ks]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const bf16x8_t b = *(const bf16x8_t *)(stg + FBM * ROWB + (ch * 64 + j * 32) * ROWB + foff[ks]);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+                }
+            }
+            if (kt == nk1 - 1) {
+                // hidden units cb * 64 + ch * 32 + (lane & 31): K piece 2 cb + ch of H
+                char *hp = hs + (2 * cb + ch) * HPIECE;
+                const int c = lane & 31;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int R = rh * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
+                    const uint32_t h2 = pack_bf16x2(silu_mul_fast(acc[0][r], acc[1][r]), 0.0f);
+                    *(uint16_t *)(hp + R * ROWB + (((c >> 3) ^ ((R >> 2) & 3)) << 4) + (c & 7) * 2) = (uint16_t)h2;
+                }
+            }
+        }
+        // phase 2: down projection from H in LDS, alpha * out into the route rows
+        wait_vmcnt<0>();
+        __syncthreads();   // H complete; the ring is free
+        issue2(0);
+        for (int st = 0; st < n2; ++st) {
+            const int nb2 = st / nk2, kt = st % nk2;
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (st + 1 < n2) issue2(st + 1);
+            if (kt == 0)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+            const char *stg = ring + (st & 1) * STAGE;
+            const char *hpc = hs + kt * HPIECE;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8_t a = *(const bf16x8_t *)(hpc + rh * 32 * ROWB + foff[ks]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const bf16x8_t b = *(const bf16x8_t *)(stg + (ch * 64 + j * 32) * ROWB + foff[ks]);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+                }
+            }
+            if (kt == nk2 - 1) {
+                float *Yr = (float *)dn.C;
+                const int ncol = nb2 * 128 + ch * 64 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = rh * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r & 3);
+                    if (m < rows) {
+                        float *yrow = Yr + (int64_t)s_route[m] * dn.ldc + ncol;
+                        const float al = s_alpha[m];
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) yrow[j * 32] = al * acc[j][r];
+                    }
+                }
+            }
+        }
+        for (int m = tid; m < rows; m += FNT) dn.done[s_route[m]] = 1;
+    }
+}
+
 template <typename TE, bool GATEUP>
 hipError_t launch_simple(const GemmArgs &a, int max_rows, hipStream_t st)
 {
@@ -847,7 +1047,30 @@ hipError_t launch_simple(const GemmArgs &a, int max_rows, hipStream_t st)
     return hipGetLastError();
 }
 
+inline hipError_t launch_fused_impl(const GemmArgs &gu, const GemmArgs &dn, int max_rows, hipStream_t st)
+{
+    if (gu.P > kGemmMaxSlots) return hipErrorInvalidValue;
+    const int64_t tiles = (max_rows + FBM - 1) / FBM + gu.P;
+    const unsigned grid = (unsigned)std::min<int64_t>(tiles, device_cus());
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fused_expert, dim3(grid), dim3(FNT), 0, st, gu, dn, (int)tiles);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool fused_expert_supported(const moe_shape &s)
+{
+    return s.dtype == MOE_DT_BF16 && s.f <= FMAXF && (s.d % 128) == 0 && (s.f % 64) == 0 && down_splits(s) == 1;
+}
+
+hipError_t launch_fused_expert(const moe_shape &s, const GemmArgs &gu, const GemmArgs &dn, int max_rows,
+                               hipStream_t st)
+{
+    if (max_rows == 0) return hipSuccess;
+    if (!fused_expert_supported(s)) return hipErrorInvalidValue;
+    return launch_fused_impl(gu, dn, max_rows, st);
+}
 
 // Tile shape of the ring kernel: tile rows, tile columns, stages, wave rows,
 // wave columns. (128- and 64-row tiles were measured slower than 256-row
