@@ -623,6 +623,58 @@ def bench_fused(args, cfg) -> int:
     return 0
 
 
+def bench_rows_curve(args, cfg, counts=(1, 8, 16, 32, 64, 128, 256, 384, 512, 768, 1024, 2048, 4096, 8192)) -> int:
+    """Expert-projection time against the number of routes one expert
+    receives (the pages' characterisation of expert latency by route count):
+    every token of a T-token prompt is routed to the same expert (top-1), so
+    one slot holds T records, and the gate/up and down kernels are timed on
+    it with HIP events. One line per route count."""
+    import numpy as np
+    import torch
+
+    from routed_expert_ffn_top_amd import binding as B
+    from routed_expert_ffn_top_amd.inputs import make_inputs
+    from routed_expert_ffn_top_amd.layer import MoELayer
+
+    base = cfg.with_(T=max(counts), k=1)
+    inp = make_inputs(base, device="cuda", residual=False)
+    layer = MoELayer(inp)
+    K = args.steps
+    rows = []
+    for R in counts:
+        s = B.make_shape(R, cfg.d, cfg.f, cfg.E, 1, cfg.n_shared, P=layer.shape.P, dtype=cfg.dtype,
+                         renorm=cfg.renorm)
+        routes, ws = B.alloc_routes(s), B.alloc_workspace(s)
+        L = torch.zeros((R, cfg.E), dtype=torch.float32, device="cuda")
+        L[:, 0] = 1.0   # every token picks expert 0
+        X = layer.X[:R]
+        B.moe_route_build(s, 0, R, L, layer.phi, 0, routes, ws)
+        for _ in range(max(args.warmup, 20)):
+            B.moe_expert_ffn(s, X, None, routes, layer.arena, layer.phi, B.MOE_FFN_EXPERTS, ws)
+        torch.cuda.synchronize()
+        for nme in ("gate_up", "down"):
+            B.moe_profile_begin(nme, K)
+        for _ in range(K):
+            B.moe_expert_ffn(s, X, None, routes, layer.arena, layer.phi, B.MOE_FFN_EXPERTS, ws)
+        torch.cuda.synchronize()
+        gu = float(np.mean(B.moe_profile_end("gate_up", K)))
+        dn = float(np.mean(B.moe_profile_end("down", K)))
+        us = (gu + dn) * 1e3
+        fl = 6.0 * R * cfg.d * cfg.f
+        rows.append({"routes": R, "gate_up_us": round(gu * 1e3, 2), "down_us": round(dn * 1e3, 2),
+                     "expert_us": round(us, 2), "us_per_route": round(us / R, 4),
+                     "tflops": round(fl / (us * 1e-6) / 1e12, 1),
+                     "weight_gbs": round(3 * cfg.d * cfg.f * 2 / (us * 1e-6) / 1e9, 1)})
+        print(json.dumps({"routes": R, **rows[-1]}), file=sys.stderr, flush=True)
+        del routes, ws
+    print(json.dumps({"metric": "expert projection time against the routes of one expert (1 GPU)",
+                      "config": {"workload": f"one expert of the {cfg.name} layer (d={cfg.d}, f={cfg.f}), bf16",
+                                 "steps": K},
+                      "curve": rows}), flush=True)
+    layer.close()
+    return 0
+
+
 def bench_stack(args, cfg, n_layers: int = 32) -> int:
     """A stack of n_layers MoE layers with independent weights (each layer's
     own seeded X, router and experts), all resident in HBM; one step runs the
@@ -687,6 +739,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--warmup-min-s", type=float, default=1.0,
                     help="keep warming up until this many seconds have passed (steady clocks)")
+    ap.add_argument("--rows-curve", action="store_true",
+                    help="time one expert's projections against the number of routes it receives")
     ap.add_argument("--fused", action="store_true",
                     help="time the fused expert tile against the two projection kernels")
     ap.add_argument("--cold", action="store_true",
@@ -751,6 +805,8 @@ def main() -> int:
         return bench_stack(args, CONFIGS[args.workload.replace("mixtral_stack_", "mixtral_")])
     if args.fused:
         return bench_fused(args, CONFIGS[args.workload])
+    if args.rows_curve:
+        return bench_rows_curve(args, CONFIGS[args.workload])
     cfg = CONFIGS[args.workload]
     inp = make_inputs(cfg, device="cuda", residual=False)
     layer = MoELayer(inp)
@@ -770,6 +826,8 @@ def main() -> int:
             ramp[20].record()
         if w_steps % 20 == 0:
             torch.cuda.synchronize()   # ties the wall-clock minimum to GPU time
+    if w_steps < 20:
+        ramp[w_steps].record()   # the end of the last of fewer than 20 warm-up steps
     torch.cuda.synchronize()
     warm_s = time.perf_counter() - w0
     ramp_ms = [ramp[i].elapsed_time(ramp[i + 1]) for i in range(min(w_steps, 20))]
