@@ -690,17 +690,20 @@ __global__ __launch_bounds__(WM *WN * 64) void k_gemm_mfma_lds(GemmArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Plain LDS-tiled kernel (fp32 FMA on the vector ALUs) for fp32 layers; also
-// runs bf16 inputs as an independent second path (its H is row-major [C][f];
-// the ring kernels' H is block-tiled, and a call always runs both
-// projections with the same kernel). 64x64 tiles, K step 16,
-// 256 threads with 4x4 outputs each. For gate/up a thread owns columns
+// Plain LDS-tiled kernel (fp32 FMA on the vector ALUs, whose fp32 peak on
+// this GPU equals the matrix cores' fp32 peak) for fp32 layers; also runs bf16
+// inputs as an independent second path (its H is row-major [C][f]; the ring
+// kernels' H is block-tiled, and a call always runs both projections with the
+// same kernel). 64x64 tiles, K step 64 (each thread has its 16 + 16 loads of a
+// step in flight at once: the layers this kernel serves are small and
+// latency-bound), 256 threads with 4x4 outputs each; every output is one fmaf
+// chain in ascending k. For gate/up a thread owns columns
 // {2tx, 2tx+1} (gate) and {32+2tx, 32+2tx+1} (up) of its 64-column block, so
 // both halves of each SwiGLU pair are in one thread.
 template <typename TE, bool GATEUP>
 __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a)
 {
-    constexpr int BM = 64, BN = 64, BK = 16;
+    constexpr int BM = 64, BN = 64, BK = 64;
     __shared__ TileInfo ti;
     __shared__ float As[BK][BM + 4];
     __shared__ float Bs[BK][BN + 4];
@@ -716,7 +719,7 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) col[j] = GATEUP ? ((j < 2) ? 2 * tx + j : 32 + 2 * tx + (j - 2)) : tx * 4 + j;
 
-    const int lr = tid >> 2, lk = (tid & 3) * 4;
+    const int lr = tid >> 2, lk = (tid & 3) * (BK / 4);
     const int rr = min(lr, rows - 1);
     const TE *ap = (GATEUP ? (const TE *)a.A + (int64_t)a.rec_token[row0 + rr] * a.lda
                            : (const TE *)a.A + (int64_t)(row0 + rr) * a.lda) + kb;
@@ -737,7 +740,7 @@ __global__ __launch_bounds__(256) void k_gemm_simple(GemmArgs a)
 
     for (int k0 = 0; k0 < K; k0 += BK) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < BK / 4; ++q) {
             const int kk = k0 + lk + q;
             As[lk + q][lr] = kk < K ? ld_f32<TE>(ap + kk) : 0.0f;
             Bs[lk + q][lr] = kk < K ? ld_f32<TE>(bslice + wtile_off(bn, kb + kk, N, a.K)) : 0.0f;
