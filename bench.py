@@ -66,6 +66,8 @@ for _t in (256, 1024, 4096):
         f"32 Mixtral-8x7B-shaped MoE layers with independent weights, all resident (90.2 GB): T={_t}, "
         "d=4096, E=8, top-2 renormalised, SwiGLU f=14336, bf16; only the MoE sublayers are timed")
 for _n in list(WORKLOAD_TEXT):
+    if _n in ("tiny_fp32", "virt_olmoe_t512", "virt_olmoe_t2048"):   # no quantised-weight variant
+        continue
     _act = WORKLOAD_TEXT[_n].replace("bf16 weights/activations", "bf16").replace(", bf16", ", bf16 activations")
     WORKLOAD_TEXT[_n + "_fp8w"] = (_act
                                    + "; expert weights stored as fp8 e4m3 codes with one fp32 scale per row "
