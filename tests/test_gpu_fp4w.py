@@ -44,6 +44,11 @@ def test_layer_olmoe_t4096_fp4w():
     _check_layer(cfg)
 
 
+def test_layer_dsv2lite_t4096_fp4w():
+    say("layer DSV2-Lite T=4096 (2 shared experts, f = 1408), MXFP4 weights, every token")
+    _check_layer(CONFIGS["dsv2lite_t4096_fp4w"])
+
+
 def test_layer_mixtral_t256_fp4w():
     say("layer Mixtral T=256, MXFP4 weights, split-K down, every token")
     cfg = CONFIGS["mixtral_t256_fp4w"]

@@ -38,6 +38,11 @@ def test_layer_olmoe_t4096_fp8w():
     _check_layer(cfg)
 
 
+def test_layer_dsv2lite_t4096_fp8w():
+    say("layer DSV2-Lite T=4096 (2 shared experts, weights not renormalised), fp8 weights, every token")
+    _check_layer(CONFIGS["dsv2lite_t4096_fp8w"])
+
+
 def test_layer_mixtral_t256_fp8w():
     say("layer Mixtral T=256, fp8 weights, split-K down, every token")
     cfg = CONFIGS["mixtral_t256_fp8w"]
