@@ -18,7 +18,7 @@ import torch
 
 from gpu_util import (OracleRun, TOL, check_descriptors, check_layer_output, check_logits,
                       check_routing_from_gpu_logits, check_y, check_topk, gpu_inputs, gpu_logits, np32, rel_err,
-                      say)
+                      sample_tokens, say)
 from oracle import oracle as oracle_mod
 from routed_expert_ffn_top_amd import binding as B
 from routed_expert_ffn_top_amd.inputs import CONFIGS, MoEConfig, make_inputs, make_logits, random_phi
@@ -264,6 +264,21 @@ def test_layer_olmoe_t4096():
     say("layer OLMoE T=4096, every token")
     cfg = CONFIGS["olmoe_t4096"]
     _check_layer(cfg)
+
+
+def test_layer_olmoe_large_T():
+    """The OLMoE-shaped layer at T = 65536: 524288 routes, so per-route rows sit
+    past 2^31 bytes into Yr and every offset into it needs 64 bits. Routing and
+    descriptors are checked for every token, outputs on 96 sampled tokens."""
+    cfg = CONFIGS["olmoe_t4096"].with_(name="olmoe_t65536", T=65536)
+    say("layer OLMoE T=65536 (Yr past 2^31 bytes), routing of every token, 96 sampled outputs")
+    inp = gpu_inputs(cfg)
+    layer = MoELayer(inp)
+    Y = inp.A.clone()
+    layer.forward(Y)
+    torch.cuda.synchronize()
+    err, ffn, _ = check_layer_output(layer, inp, Y, tokens=sample_tokens(cfg.T, 96))
+    say(f"  rel err {err:.3e}, expert sum {ffn:.3e}")
 
 
 def test_layer_mixtral_t4096():
