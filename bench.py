@@ -212,14 +212,15 @@ def layer_algorithmic(cfg) -> dict:
     once, each output written once)."""
     T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f
     kp = k + cfg.n_shared
+    ne = E + cfg.n_shared   # expert slices read: the routed experts and the shared ones
     R = T * kp
     return {
         "router": (T * d * 2 + E * d * 4 + T * E * 4, 2.0 * T * E * d),
         "top-k": (T * E * 4 + T * kp * 8, 0.0),
         "route count": (R * 4, 0.0),
         "route place": (R * 4 + R * 12, 0.0),
-        "gate/up": (E * 2 * f * d * 2 + R * d * 2 + R * f * 2, 4.0 * R * d * f),
-        "down": (E * d * f * 2 + R * f * 2 + R * d * 4, 2.0 * R * d * f),
+        "gate/up": (ne * 2 * f * d * 2 + R * d * 2 + R * f * 2, 4.0 * R * d * f),
+        "down": (ne * d * f * 2 + R * f * 2 + R * d * 4, 2.0 * R * d * f),
         "combine": (R * d * 4 + 2 * T * d * 4, 0.0),
     }
 
