@@ -372,6 +372,23 @@ def test_edge_shapes():
     assert Y.shape == (0, MID.d)
 
 
+# The largest expert table the library takes: 256 routed experts plus 2 shared
+# ones (E <= 256, E + shared <= 512), placed at random into 512 physical slots
+# (the expert kernels keep at most 512 slot entries on chip), top-8 over a few
+# hundred tokens, so that most slots hold one small row block.
+MAX_EXP = MoEConfig(name="max_experts", index=81, T=400, d=128, f=128, E=256, k=8, n_shared=2, renorm=False)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "bf16_fp8w", "bf16_fp4w"])
+def test_layer_max_experts_and_slots(dtype):
+    cfg = MAX_EXP.with_(dtype=dtype, name=f"max_experts_{dtype}")
+    say(f"largest expert table: {cfg.E} + {cfg.n_shared} experts in 512 slots ({dtype})")
+    phi = random_phi(cfg.n_exp, 512, seed=17).tolist()
+    _, layer, _ = _check_layer(cfg, phi=phi, P=512)
+    counts = layer.routes["slot_count"].cpu().numpy()
+    assert counts.shape == (512,) and int((counts > 0).sum()) > 200
+
+
 @pytest.mark.parametrize("cfg,padx,pady", [(MID, 72, 36), (CONFIGS["tiny_fp32"], 12, 4)], ids=["bf16", "fp32"])
 def test_layer_row_strides(cfg, padx, pady):
     """X and Y with row strides wider than d: the same bits as the contiguous
