@@ -678,6 +678,90 @@ def bench_rows_curve(args, cfg, counts=(1, 8, 16, 32, 64, 128, 256, 384, 512, 76
     return 0
 
 
+def bench_ep_share(args, cfg, n: int) -> int:
+    """One GPU's share of the layer under n-way expert parallelism, run on
+    this GPU at its real shape. The whole prompt is routed (router, top-k) as
+    on every GPU; the route map and the expert FFN then see a placement map
+    that holds only this share's routed experts (E/n consecutive ids) and
+    leaves the rest absent, so the kernels work on exactly the records the
+    share owns. Shared experts, replicated on every GPU, are run token
+    parallel: each GPU runs them for its own T/n tokens (a second route build
+    over that token range with a map that holds only the shared experts).
+    The exchange of rows between GPUs and the combine of the returned rows
+    are not run. Each share is timed in turn; the slowest bounds the layer."""
+    import numpy as np
+    import torch
+
+    from routed_expert_ffn_top_amd import binding as B
+    from routed_expert_ffn_top_amd.inputs import make_inputs
+    from routed_expert_ffn_top_amd.layer import MoELayer
+
+    if cfg.E % n or cfg.T % n:
+        raise SystemExit(f"--ep-share {n}: {cfg.E} experts or {cfg.T} tokens do not split evenly")
+    inp = make_inputs(cfg, device="cuda", residual=False)
+    layer = MoELayer(inp)
+    s = layer.shape
+    L = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+    B.moe_router_logits(s, layer.X, layer.Wr, layer.bias, L)
+    K = args.steps
+    per, tpg = cfg.E // n, cfg.T // n
+    ws2 = B.alloc_workspace(s) if cfg.n_shared else None
+    routes2 = B.alloc_routes(s) if cfg.n_shared else None
+
+    def tiles_of(counts):
+        return int(sum(-(-int(c) // 256) for c in counts)) * (-(-2 * cfg.f // 256))
+
+    shares = []
+    for r in range(n):
+        phi = [slot if r * per <= e < (r + 1) * per else -1 for e, slot in enumerate(layer.phi)]
+        B.moe_route_build(s, 0, s.T, L, phi, 0, layer.routes, layer.ws)
+        calls = [(phi, layer.routes, layer.ws)]
+        if cfg.n_shared:
+            phi_s = [slot if e >= cfg.E else -1 for e, slot in enumerate(layer.phi)]
+            B.moe_route_build(s, r * tpg, tpg, L, phi_s, 0, routes2, ws2)
+            calls.append((phi_s, routes2, ws2))
+
+        def ffn():
+            for ph, rt, w in calls:
+                B.moe_expert_ffn(s, layer.X, None, rt, layer.arena, ph, B.MOE_FFN_EXPERTS, w)
+
+        w0, m = time.perf_counter(), 0
+        while m < args.warmup or time.perf_counter() - w0 < args.warmup_min_s:
+            ffn()
+            m += 1
+            if m % 20 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        for nme in ("gate_up", "down"):
+            B.moe_profile_begin(nme, K * len(calls))
+        for _ in range(K):
+            ffn()
+        torch.cuda.synchronize()
+        gu = float(np.sum(B.moe_profile_end("gate_up", K * len(calls)))) / K
+        dn = float(np.sum(B.moe_profile_end("down", K * len(calls)))) / K
+        R = sum(int(rt["slot_count"].cpu().numpy().sum()) for _, rt, _ in calls)
+        fl = 6.0 * R * cfg.d * cfg.f
+        shares.append({"share": r, "routes": R, "gate_up_tiles": sum(tiles_of(rt["slot_count"].cpu().numpy())
+                                                                     for _, rt, _ in calls),
+                       "gate_up_ms": round(gu, 4), "down_ms": round(dn, 4), "expert_ffn_ms": round(gu + dn, 4),
+                       "tflops": round(fl / ((gu + dn) * 1e-3) / 1e12, 1)})
+        print(json.dumps(shares[-1]), file=sys.stderr, flush=True)
+    worst = max(shares, key=lambda x: x["expert_ffn_ms"])
+    out = {"metric": f"expert FFN of one GPU's share under {n}-way expert parallelism, run on 1 GPU",
+           "config": {"workload": WORKLOAD_TEXT[args.workload], "experts_per_share": per,
+                      "shared_experts": f"{cfg.n_shared}, run for each share's {tpg} tokens" if cfg.n_shared else 0,
+                      "steps": K},
+           "shares": shares,
+           "slowest_share": worst["share"],
+           "slowest_share_ms": worst["expert_ffn_ms"],
+           "slowest_share_tflops": worst["tflops"],
+           "routes_total": sum(x["routes"] for x in shares),
+           "not_run": "the all-to-all exchange of X rows and Yr rows, the combine"}
+    print(json.dumps(out), flush=True)
+    layer.close()
+    return 0
+
+
 def bench_stack(args, cfg, n_layers: int = 32) -> int:
     """A stack of n_layers MoE layers with independent weights (each layer's
     own seeded X, router and experts), all resident in HBM; one step runs the
@@ -746,6 +830,8 @@ def main() -> int:
                     help="time one expert's projections against the number of routes it receives")
     ap.add_argument("--fused", action="store_true",
                     help="time the fused expert tile against the two projection kernels")
+    ap.add_argument("--ep-share", type=int, default=0, metavar="N",
+                    help="time each GPU's share of the expert FFN under N-way expert parallelism, on this GPU")
     ap.add_argument("--cold", action="store_true",
                     help="also time layers with a 512 MB scratch write before each (cold caches)")
     ap.add_argument("--workload", default="olmoe_t4096", choices=sorted(WORKLOAD_TEXT))
@@ -810,6 +896,8 @@ def main() -> int:
         return bench_fused(args, CONFIGS[args.workload])
     if args.rows_curve:
         return bench_rows_curve(args, CONFIGS[args.workload])
+    if args.ep_share:
+        return bench_ep_share(args, CONFIGS[args.workload], args.ep_share)
     cfg = CONFIGS[args.workload]
     inp = make_inputs(cfg, device="cuda", residual=False)
     layer = MoELayer(inp)
