@@ -312,6 +312,34 @@ def test_deterministic_and_phi_independent():
     assert torch.equal(_layer_out(moved, inp), y1), "a different placement changed the output"
 
 
+def test_two_layers_concurrently_on_two_streams():
+    """Two independent layers (each with its own inputs, arena, descriptors
+    and workspace) enqueued alternately on two streams, four times each with
+    no synchronisation in between, give the bits each gives alone: a call
+    keeps no state outside the caller's buffers and its own arena."""
+    say("two layers on two streams")
+    cfgs = [MID, MID_SHARED]
+    layers, inps, ref = [], [], []
+    for cfg in cfgs:
+        inp = gpu_inputs(cfg)
+        layer = MoELayer(inp)
+        layers.append(layer)
+        inps.append(inp)
+        ref.append(_layer_out(layer, inp))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    for _ in range(4):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                Y = inps[i].A.clone()
+                layers[i].forward(Y, compute=streams[i])
+                outs[i].append(Y)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r, Y in enumerate(outs[i]):
+            assert torch.equal(Y.view(torch.int32), ref[i].view(torch.int32)), f"layer {i} run {r} differs"
+
+
 def test_partial_phi_leaves_out_absent_experts():
     say("partial placement map")
     inp = gpu_inputs(MID)
