@@ -4,9 +4,11 @@
 // * (W_u x))).
 //
 // Work is a list of tiles (slot s, BM consecutive records of s, BN columns of
-// the slot's weight slice). Each workgroup finds its tile from the per-slot
-// record offsets, so the grid is launched for an upper bound and surplus
-// workgroups leave at once; nothing is read back to the host.
+// the slot's weight slice), decoded on the device from the per-slot record
+// offsets, so nothing is read back to the host. The ring kernel is persistent
+// (as many workgroups as fit on the GPU at once, each walking its tiles); the
+// plain kernel is launched for an upper bound on the tile count and surplus
+// workgroups leave at once.
 //
 //  gate/up: A = X rows gathered by rec_token (K = d), B = the slot's packed
 //           [2f][d] gate/up slice, whose rows alternate 32 gate / 32 up, so a
