@@ -33,6 +33,13 @@
  *    expert, K' = k + n_shared. Ranks 0..k-1 are the routed top-k in
  *    descending logit order; ranks k..K'-1 are the shared experts
  *    E..E+n_shared-1 with weight 1.
+ *  - Concurrency: calls with their own workspace and descriptors may be in
+ *    flight on different streams at once. A workspace or a descriptor set
+ *    used by two calls on different streams must be ordered by the caller
+ *    (same stream, or events). An arena may be used from several streams
+ *    and host threads: its residency table is updated under a lock and
+ *    orders loads into a slot after the slot's last use with events.
+ *    moe_last_error() reports the calling host thread's last error.
  */
 #ifndef ROUTED_EXPERT_FFN_MOE_H
 #define ROUTED_EXPERT_FFN_MOE_H
