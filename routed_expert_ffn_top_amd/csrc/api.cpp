@@ -203,7 +203,7 @@ struct HipBackend {
 }  // namespace
 
 struct moe_arena {
-    std::mutex mu;
+    mutable std::mutex mu;   // guards the residency table
     moe_shape shape;
     char *plane_gu;
     char *plane_d;
@@ -646,6 +646,7 @@ moe_status arena_phi(const moe_arena *a, int32_t *phi, int32_t n)
     if (!a || !phi) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
     const int ne = a->shape.E + a->shape.n_shared;
     if (n < ne) return fail(MOE_ERR_INVALID_ARG, "phi needs %d entries", ne);
+    std::lock_guard<std::mutex> lk(a->mu);
     a->res.placement(phi, n);
     return MOE_OK;
 }
@@ -654,6 +655,7 @@ moe_status arena_slot_info(const moe_arena *a, int32_t slot, int32_t *state, int
 {
     if (!a) return fail(MOE_ERR_INVALID_ARG, "arena is NULL");
     if (slot < 0 || slot >= a->shape.P) return fail(MOE_ERR_INVALID_ARG, "slot %d outside [0, P)", slot);
+    std::lock_guard<std::mutex> lk(a->mu);
     if (state) *state = a->res.state(slot);
     if (expert) *expert = a->res.owner(slot);
     return MOE_OK;
@@ -746,14 +748,15 @@ moe_status layer_prefill_resident(const moe_shape *shape, const void *X, const f
         HIP_TRY(TIMED(MOE_KERNEL_ROUTER, cs, launch_router_logits(s, X, W_r, bias, ws_at<float>(ws, w.logits), cs)),
                 "router launch");
     }
-    // every expert must be Ready in the arena
-    MOE_TRY(arena_phi(arena, phi, ne));
+    const int tc = (int)std::min<int64_t>(s.T, s.capacity / kp);
+    if (s.T > 0 && tc < 1) return fail(MOE_ERR_CAPACITY, "capacity %d below one token's %d routes", s.capacity, kp);
+    // every expert must be Ready in the arena; the placement is read and
+    // used under the arena's lock
+    std::lock_guard<std::mutex> lk(arena->mu);
+    arena->res.placement(phi, ne);
     for (int e = 0; e < ne; ++e)
         if (phi[e] < 0) return fail(MOE_ERR_SLOT_STATE, "expert %d is not resident", e);
     MOE_TRY(check_phi(shape, phi, &pa));
-    const int tc = (int)std::min<int64_t>(s.T, s.capacity / kp);
-    if (s.T > 0 && tc < 1) return fail(MOE_ERR_CAPACITY, "capacity %d below one token's %d routes", s.capacity, kp);
-    std::lock_guard<std::mutex> lk(arena->mu);
     MOE_TRY(arena_acquire(arena, phi, cs));
     for (int t0 = 0; t0 < s.T; t0 += tc) {
         const int nt = std::min(tc, s.T - t0);
